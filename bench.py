@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Throughput of the bit-exact block-scaled int8 GEMM path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mlp|head|w1|step]
+
+One step is one pass of the whole path over one batch: per GEMM,
+quantize_rows of the left operand, quantize_cols of the right one, and the
+int8 GEMM with its fused epilogue and output hash.  The default workload is
+the GPT-2-small MLP (batch 8 x sequence 1024 = 8192 token rows): the
+up-projection 8192x768 @ 768x3072 with ReLU, then the down-projection
+8192x3072 @ 3072x768 on its output.  Inputs are seeded synthetic f32
+tensors, resident in HBM before timing starts.
+
+Prints ONE JSON line: value = int8 GEMM operations (2MNK summed over the
+step's GEMMs) per second of the whole step, in TOPS; `roofline` for the
+step's dominant kernel from HIP events recorded around every launch of the
+timed steps; `cpu_baseline` = the CPU oracle timed on this host on a full
+step; `parity` = whether the oracle's output hashes equal the GPU's.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, tera-ops/s
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+RIDGE = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # ops per byte
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workloads: lists of GEMMs (name, A-source, B-source, relu); the GPU step and
+# the oracle step walk the same list
+# ---------------------------------------------------------------------------
+def make_workload(name):
+    from synth import inputs as S
+    if name == "mlp":
+        X, Wu, Wd = S.w2_inputs()
+        desc = ("GPT-2-small MLP: up 8192x768 @ 768x3072 (ReLU), then down "
+                "8192x3072 @ 3072x768 on the up output; quantize passes included")
+        gemms = [("up", "X", "Wu", True, "H"), ("down", "H", "Wd", False, None)]
+        return desc, {"X": X, "Wu": Wu, "Wd": Wd}, gemms
+    if name == "head":
+        X, Wh = S.w3_fwd_inputs()
+        _, dY = S.w3_wgrad_inputs()
+        desc = ("GPT-2-small LM head: forward 8192x768 @ 768x50304 and weight "
+                "gradient X^T (768x8192) @ dY (8192x50304); quantize passes included")
+        gemms = [("head_fwd", "X", "Wh", False, None), ("head_wgrad", "X^T", "dY", False, None)]
+        return desc, {"X": X, "Wh": Wh, "dY": dY}, gemms
+    if name == "w1":
+        A, B = S.w1_inputs()
+        return "single 256x256x256 GEMM", {"A": A, "B": B}, [("w1", "A", "B", False, None)]
+    raise SystemExit(f"unknown workload {name}")
+
+
+def gemm_mnk(tensors, a_src, b_src):
+    if a_src.endswith("^T"):
+        a = tensors[a_src[:-2]]
+        M, K = a.shape[1], a.shape[0]
+    else:
+        M, K = tensors[a_src].shape
+    N = tensors[b_src].shape[1]
+    return M, N, K
+
+
+# ---------------------------------------------------------------------------
+# GPU step with preallocated buffers and direct C-ABI calls
+# ---------------------------------------------------------------------------
+class GpuStep:
+    def __init__(self, g, torch, tensors, gemms):
+        self.g, self.torch, self.lib = g, torch, g.load()
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        self.stream = torch.cuda.current_stream(dev)
+        self.sp = self.stream.cuda_stream
+        self.t = {k: torch.from_numpy(v).to(dev) for k, v in tensors.items()}
+        self.gemms = []
+        ws_bytes = 256
+        shapes = {k: tuple(v.shape) for k, v in tensors.items()}
+        for (name, a_src, b_src, relu, out_name) in gemms:
+            if a_src.endswith("^T"):
+                K, M = shapes[a_src[:-2]]
+                a_mode, a_key = "cols", a_src[:-2]
+            else:
+                M, K = shapes[a_src]
+                a_mode, a_key = "rows", a_src
+            N = shapes[b_src][1]
+            shapes[out_name or name] = (M, N)
+            ld = (K + 15) // 16 * 16
+            e = dict(name=name, M=M, N=N, K=K, relu=relu, a_mode=a_mode, a_key=a_key, b_key=b_src,
+                     out=out_name or name,
+                     QA=torch.empty((M, ld), dtype=torch.int8, device=dev),
+                     sA=torch.empty(M, dtype=torch.float32, device=dev),
+                     QB=torch.empty((N, ld), dtype=torch.int8, device=dev),
+                     sB=torch.empty(N, dtype=torch.float32, device=dev),
+                     C=torch.empty((M, N), dtype=torch.float32, device=dev),
+                     h=torch.zeros(1, dtype=torch.int64, device=dev), ld=ld)
+            self.t[e["out"]] = e["C"]
+            ws_bytes = max(ws_bytes, g.workspace_bytes(M, N, K))
+            self.gemms.append(e)
+        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        self.events = None
+
+    def _q(self, mode, X, Q, s, ld):
+        rows, cols = X.shape
+        fn = self.lib.quantize_rows if mode == "rows" else self.lib.quantize_cols
+        rc = fn(X.data_ptr(), rows, cols, X.stride(0), Q.data_ptr(), ld, s.data_ptr(), self.sp)
+        if rc:
+            raise RuntimeError(self.lib.i8g_status_string(rc).decode())
+
+    def run(self, record=None):
+        lib = self.lib
+        for e in self.gemms:
+            marks = []
+            ev = self.torch.cuda.Event
+            if record is not None:
+                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
+            self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])
+            if record is not None:
+                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
+            self._q("cols", self.t[e["b_key"]], e["QB"], e["sB"], e["ld"])
+            if record is not None:
+                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
+            flags = (1 if e["relu"] else 0) | 2
+            rc = lib.gemm_i8_blockscaled(e["QA"].data_ptr(), e["ld"], e["sA"].data_ptr(),
+                                         e["QB"].data_ptr(), e["ld"], e["sB"].data_ptr(),
+                                         e["M"], e["N"], e["K"], e["C"].data_ptr(), e["N"], flags,
+                                         e["h"].data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                                         self.sp)
+            if rc:
+                raise RuntimeError(lib.i8g_status_string(rc).decode())
+            if record is not None:
+                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
+                record.append((e, marks))
+
+    def hashes(self):
+        return [self.g.hash_value(e["h"]) for e in self.gemms]
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle step (the cpu_baseline leg)
+# ---------------------------------------------------------------------------
+def oracle_step(tensors, gemms):
+    import numpy as np
+    from oracle import hashref, ref
+    t = dict(tensors)
+    hashes = []
+    for (name, a_src, b_src, relu, out_name) in gemms:
+        if a_src.endswith("^T"):
+            QA, sA = ref.quantize_cols(t[a_src[:-2]])
+        else:
+            QA, sA = ref.quantize_rows(t[a_src])
+        QB, sB = ref.quantize_cols(t[b_src])
+        C = ref.gemm_i8_blockscaled(QA, sA, QB, sB, relu)
+        t[out_name or name] = C
+        hashes.append(hashref.output_hash(C))
+        del QA, QB
+    return hashes
+
+
+def cpu_baseline(tensors, gemms, ops, budget_s=10.0):
+    from threadpoolctl import threadpool_info
+    blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+    threads = max([d.get("num_threads", 1) for d in blas] or [1])
+    times, hashes = [], None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        hashes = oracle_step(tensors, gemms)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 3:
+            break
+    sec = statistics.median(times)
+    return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} full step(s) of the same workload, median {sec:.2f} s; "
+                      f"numpy float32 per-op quantize/epilogue (1 thread), float64 BLAS "
+                      f"contraction ({threads} threads), numpy uint64 hash"}, hashes
+
+
+# ---------------------------------------------------------------------------
+# traffic from committed PMC summaries (null unless the kernels are unchanged)
+# ---------------------------------------------------------------------------
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int8_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_sha") != kernel_source_sha():
+        return None
+    ent = data.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "w1"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(its sharding is described in DESIGN.md); rerun with --gpus 1", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import int8_gemm_amd as g
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"[bench] workload {a.workload}: generating inputs")
+    desc, tensors, gemms = make_workload(a.workload)
+    step = GpuStep(g, torch, tensors, gemms)
+    ops = sum(2.0 * e["M"] * e["N"] * e["K"] for e in step.gemms)
+    log(f"[bench] {len(step.gemms)} GEMMs, {ops / 1e9:.2f} GOP per step; warmup {a.warmup}")
+    for _ in range(a.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    gpu_hashes = step.hashes()
+
+    # timed region: exactly K steps, events around every call
+    record = []
+    log(f"[bench] timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(step.stream)
+    for _ in range(a.steps):
+        step.run(record)
+    stop.record(step.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = gpu_ms / a.steps
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.4f} ms/step (wall {wall / a.steps * 1e3:.4f} ms/step), {value:.1f} TOPS")
+
+    # per-call durations (us) from the events of the timed steps
+    per = {}
+    for e, m in record:
+        for label, i in (("quantize_A", 0), ("quantize_B", 1), ("gemm", 2)):
+            per.setdefault((e["name"], label), []).append(m[i].elapsed_time(m[i + 1]) * 1e3)
+    kernels = []
+    for (name, label), us in per.items():
+        e = next(x for x in step.gemms if x["name"] == name)
+        avg = statistics.mean(us)
+        M, N, K = e["M"], e["N"], e["K"]
+        if label == "gemm":
+            gops = 2.0 * M * N * K
+            nbytes = M * K + N * K + 4 * M + 4 * N + 4 * M * N + 8
+            bound = "mfma" if gops / nbytes >= RIDGE else "hbm"
+            shape = f"{M}x{N}x{K}"
+        else:
+            rows, cols = (M, K) if label == "quantize_A" else (K, N)
+            if label == "quantize_A" and e["a_mode"] == "cols":
+                rows, cols = K, M
+            gops, nbytes, bound = 0.0, 5 * rows * cols + 4 * (cols if label == "quantize_B" or e["a_mode"] == "cols" else rows), "hbm"
+            shape = f"{rows}x{cols} ({'cols' if label == 'quantize_B' or e['a_mode'] == 'cols' else 'rows'})"
+        if bound == "mfma":
+            ach, peak, unit = gops / (avg * 1e-6) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = nbytes / (avg * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s"
+        kernels.append({"call": f"{name}.{label}", "shape": shape, "avg_us": round(avg, 2),
+                        "total_us_per_step": round(avg, 2), "bound": bound,
+                        "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                        "frac": round(ach / peak, 4), "algorithmic_bytes": nbytes,
+                        "int8_ops": gops,
+                        "tops": round(gops / (avg * 1e-6) / 1e12, 1) if gops else None})
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    roof = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+            "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic_for(dom["call"]),
+            "kernel": dom["call"], "shape": dom["shape"], "avg_us": dom["avg_us"]}
+
+    cpu = None
+    parity = None
+    if not a.no_cpu_baseline:
+        log("[bench] cpu_baseline: oracle on the host")
+        cpu, cpu_hashes = cpu_baseline(tensors, gemms, ops)
+        parity = cpu_hashes == gpu_hashes
+        log(f"[bench] oracle {cpu['value']:.4f} TOPS, parity {parity}")
+
+    out = {
+        "metric": "bit-exact block-scaled int8 GEMM TOPS (% of int8 MFMA peak), GPT-2-small shapes",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": desc, "name": a.workload,
+                   "gemms": [f"{e['M']}x{e['N']}x{e['K']}{' relu' if e['relu'] else ''}"
+                             for e in step.gemms],
+                   "int8_ops_per_step": ops, "batch": 8, "seq_len": 1024, "tokens": 8192},
+        "pct_of_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "gpu_hashes": [f"{h:#018x}" for h in gpu_hashes],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

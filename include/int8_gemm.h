@@ -1,0 +1,170 @@
+/*
+ * int8_gemm.h -- bit-reproducible block-scaled int8 GEMM for AMD Instinct
+ * MI355X (gfx950).  C ABI of libint8_gemm.so.
+ *
+ * The method is the one of the DaisyChain-Train page "Verification -- why
+ * you can trust the numbers", section "The verified INT8 units":
+ *   1. A (M x K) is quantized per row and B (K x N) per column with
+ *      scale = max(|line|)/127 floored at 1e-8, values to int8;
+ *   2. int8 products are accumulated exactly in int32;
+ *   3. the f32 epilogue rounds after the int->float conversion and after
+ *      each multiply: out = f32(f32(f32(acc) * s_row[i]) * s_col[j]).
+ * Every device that follows these steps, and a plain CPU, produce the same
+ * output bytes, so outputs can be compared by hashing them (the page's
+ * opening paragraph and "Layer 3: the kernel probe").
+ *
+ * Rounding is binary32 round-to-nearest-even throughout.  The readings this
+ * library takes where the page leaves a step open:
+ *   s   = max(RN(a / 127), RN(1e-8))      a = max |x| over the line,
+ *                                         RN(1e-8) = 0x322BCC77, division
+ *                                         correctly rounded
+ *   inv = RN(1 / s)                       correctly rounded
+ *   q   = floor(RN(RN(x * inv) + 0.5))    two roundings, never fused;
+ *                                         q is in [-127, 127]
+ *   out = RN(RN(RN(acc) * s_row[i]) * s_col[j]), row scale first;
+ *   ReLU (optional, fused): out = out > 0 ? out : +0.0.
+ *
+ * Conventions for every entry point
+ *   - All array pointers are DEVICE pointers (memory from hipMalloc or a
+ *     PyTorch tensor on the current device), owned by the caller; the
+ *     library keeps no reference to them after the call is enqueued.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and runs asynchronously; nothing is synchronized.
+ *   - Sizes are int64_t element counts; leading dimensions (ld*) are in
+ *     elements of the array they describe, row-major.
+ *   - The return value is a status code (I8G_OK = 0).  On a non-zero
+ *     status nothing has been enqueued, except for I8G_EHIP, which reports
+ *     a launch failure from the HIP runtime.  Nothing is printed and no
+ *     C++ exception crosses the ABI.
+ *   - Inputs must be finite (no NaN or infinity); other inputs give
+ *     unspecified bytes.
+ *   - Empty shapes (a zero dimension) are valid and enqueue nothing except
+ *     the hash of an empty output where one is requested.
+ *   - The library allocates no device memory.  Calls that share a
+ *     workspace must be ordered (same stream, or synchronized).
+ */
+#ifndef INT8_GEMM_H
+#define INT8_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define I8G_OK          0  /* success                                        */
+#define I8G_EINVAL      1  /* null pointer, negative size, ld < row length   */
+#define I8G_EKRANGE     2  /* K > 133144: int32 accumulation could overflow  */
+#define I8G_EALIGN      3  /* a GEMM operand's pointer or ld not 16-byte     */
+                           /* aligned, or ld below K rounded up to 16        */
+#define I8G_EWORKSPACE  4  /* workspace missing or smaller than required     */
+#define I8G_EHIP        5  /* the HIP runtime reported a launch error        */
+
+/* flags of gemm_i8_blockscaled */
+#define I8G_RELU 1u        /* fused ReLU: out = out > 0 ? out : +0          */
+#define I8G_HASH 2u        /* also write the output hash to *hash            */
+
+/* Largest K for which |acc| <= 127*127*K stays below 2^31. */
+#define I8G_K_MAX 133144
+
+/*
+ * quantize_rows -- per-row quantization (step 1 of "The verified INT8
+ * units", applied to the rows of an operand).
+ *   X      rows x cols f32, row-major, leading dimension ldx >= cols.
+ *   Q      rows x cols int8 output, leading dimension ldq >= cols; bytes in
+ *          columns [cols, ldq) are not written.
+ *   scale  rows f32 output: scale[i] = max(RN(max_k |X[i,k]|/127), RN(1e-8)).
+ * Q[i,k] = floor(RN(RN(X[i,k] * RN(1/scale[i])) + 0.5)).
+ * With cols == 0 only the scales are written (each is RN(1e-8)).
+ * Any alignment of X and Q is accepted (16-byte aligned rows are faster).
+ * Errors: I8G_EINVAL (null pointer with rows*cols > 0, null scale with
+ * rows > 0, negative size, ldx < cols, ldq < cols), I8G_EHIP.
+ */
+int quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                  int8_t* Q, int64_t ldq, float* scale, void* stream);
+
+/*
+ * quantize_cols -- per-column quantization with a transposed int8 output,
+ * so that both GEMM operands are contiguous along K.
+ *   X      rows x cols f32, row-major, leading dimension ldx >= cols.
+ *   Qt     cols x rows int8 output (the transpose), leading dimension
+ *          ldqt >= rows; bytes in columns [rows, ldqt) are not written.
+ *   scale  cols f32 output: scale[j] = max(RN(max_k |X[k,j]|/127), RN(1e-8)).
+ *          It is also used as scratch while the call runs.
+ * Qt[j,k] = floor(RN(RN(X[k,j] * RN(1/scale[j])) + 0.5)).
+ * With rows == 0 only the scales are written (each is RN(1e-8)).
+ * Errors: as quantize_rows (with the roles of rows and cols exchanged).
+ */
+int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                  int8_t* Qt, int64_t ldqt, float* scale, void* stream);
+
+/*
+ * gemm_i8_blockscaled -- C = epilogue(QA . QBt^T) (steps 2 and 3 of "The
+ * verified INT8 units").
+ *   QA     M x K int8, row-major (K contiguous), leading dimension lda.
+ *   s_row  M f32 row scales of A.
+ *   QBt    N x K int8, row-major (K contiguous): B's quantized columns as
+ *          rows, leading dimension ldb.
+ *   s_col  N f32 column scales of B.
+ *   C      M x N f32 output, row-major, leading dimension ldc >= N.
+ *   flags  I8G_RELU and/or I8G_HASH.
+ *   hash   device pointer to one uint64_t, required with I8G_HASH (else
+ *          ignored): receives output_hash(C) for this output.
+ *   workspace, workspace_bytes
+ *          device scratch of at least gemm_i8_workspace_bytes(M, N, K)
+ *          bytes, 256-byte aligned.  It must be zero-filled before its
+ *          first use.  Every call that completes returns its control words
+ *          (the 256-byte header and the per-tile tickets after it) to zero,
+ *          so one zeroed buffer serves any sequence of ordered calls; the
+ *          rest is scratch (int32 partial tiles) with unspecified contents.
+ * acc[i,j] = sum_k QA[i,k]*QBt[j,k] is exact (int32); the K range may be
+ * split across workgroups, which cannot change a byte since integer
+ * addition is associative.
+ * out[i,j] = RN(RN(RN(acc[i,j]) * s_row[i]) * s_col[j]) (then ReLU).
+ * Requirements: QA and QBt 16-byte aligned, lda and ldb multiples of 16 and
+ * >= K rounded up to 16 (bytes k >= K of each row are read but ignored);
+ * every QA row is readable for lda bytes and every QBt row for ldb bytes.
+ * Errors: I8G_EINVAL, I8G_EKRANGE (K > I8G_K_MAX), I8G_EALIGN,
+ * I8G_EWORKSPACE, I8G_EHIP.
+ */
+int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row,
+                        const int8_t* QBt, int64_t ldb, const float* s_col,
+                        int64_t M, int64_t N, int64_t K,
+                        float* C, int64_t ldc, uint32_t flags, uint64_t* hash,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256). */
+size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * output_hash -- the probe hash of an M x N f32 matrix (the page's "Layer
+ * 3: the kernel probe"; the page names no function, this library defines):
+ *   bits(i,j) = 32-bit pattern of C[i,j]           (-0 and +0 differ)
+ *   r(i)      = 2*mix31(i mod 2^31) + 1            (mix31: a bijection of
+ *               [0,2^31): x ^= x>>16; x *= 0x3B9C5A1D; x ^= x>>13;
+ *               x *= 0x2F6E8B35; x ^= x>>16, products mod 2^31)
+ *   c(j)      = fmix64(j + 0x9E3779B97F4A7C15) | 1  (MurmurHash3 finalizer)
+ *   S         = sum_{i,j} c(j) * r(i) * bits(i,j)   mod 2^64
+ *   H         = fmix64(S ^ fmix64(M * 2^32 + N))
+ *   C      M x N f32, leading dimension ldc >= N; M, N < 2^31.
+ *   hash   device pointer to one uint64_t that receives H.
+ *   workspace  as for gemm_i8_blockscaled (any buffer of >= 256 zeroed
+ *          bytes; left zeroed).
+ * Errors: I8G_EINVAL, I8G_EWORKSPACE, I8G_EHIP.
+ */
+int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
+                uint64_t* hash, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* i8g_status_string(int status);
+
+/* Library version, e.g. "int8_gemm 0.1.0 gfx950". */
+const char* i8g_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* INT8_GEMM_H */

@@ -1,0 +1,201 @@
+"""Python binding of libint8_gemm.so (bit-reproducible block-scaled int8 GEMM).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  The
+entry points have the names of the C ABI in ``include/int8_gemm.h``:
+
+    quantize_rows(X)                 -> (Q, scale)      per-row, Q is rows x cols
+    quantize_cols(X)                 -> (Qt, scale)     per-column, Qt is cols x rows
+    gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False)
+                                     -> C  or  (C, hash_tensor)
+    output_hash(C)                   -> hash_tensor     (1 element, device)
+    blockscaled_gemm(A, B, relu=False, want_hash=False)  A @ B, all steps
+
+Hash tensors hold the 64-bit hash in an int64 element; ``hash_value``
+returns it as a Python int in [0, 2^64).  If the library is not built, or
+cannot be loaded, every entry point raises: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "output_hash",
+           "blockscaled_gemm", "hash_value", "workspace_bytes", "library_path", "load",
+           "I8G_RELU", "I8G_HASH", "K_MAX", "I8GError"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libint8_gemm.so")
+I8G_RELU = 1
+I8G_HASH = 2
+K_MAX = 133144
+EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_workspace_bytes",
+            "output_hash", "i8g_status_string", "i8g_version")
+
+_lib = None
+_ws = {}
+
+
+class I8GError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__(f"int8_gemm status {status}: {text}")
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load libint8_gemm.so (once).  torch is imported first so that the
+    library binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m int8_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_LOCAL)
+    c_i64, c_vp, c_u32, c_sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_size_t
+    lib.quantize_rows.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]
+    lib.quantize_rows.restype = ctypes.c_int
+    lib.quantize_cols.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]
+    lib.quantize_cols.restype = ctypes.c_int
+    lib.gemm_i8_blockscaled.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
+                                        c_vp, c_i64, c_u32, c_vp, c_vp, c_sz, c_vp]
+    lib.gemm_i8_blockscaled.restype = ctypes.c_int
+    lib.gemm_i8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
+    lib.gemm_i8_workspace_bytes.restype = c_sz
+    lib.output_hash.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    lib.output_hash.restype = ctypes.c_int
+    lib.i8g_status_string.argtypes = [ctypes.c_int]
+    lib.i8g_status_string.restype = ctypes.c_char_p
+    lib.i8g_version.argtypes = []
+    lib.i8g_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise I8GError(rc, load().i8g_status_string(rc).decode())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _req_matrix(x, dtype, name):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if x.size(1) > 1 and x.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+
+
+def _ld(x):
+    return max(x.stride(0), x.size(1), 1)
+
+
+def _round16(n):
+    return (n + 15) // 16 * 16
+
+
+def _int8_padded(rows, cols, device):
+    """rows x cols int8 view of a buffer whose rows are padded to 16 bytes."""
+    ld = max(_round16(cols), 16)
+    return torch.empty((rows, ld), dtype=torch.int8, device=device)[:, :cols]
+
+
+def quantize_rows(X):
+    _req_matrix(X, torch.float32, "X")
+    rows, cols = X.shape
+    Q = _int8_padded(rows, cols, X.device)
+    s = torch.empty(rows, dtype=torch.float32, device=X.device)
+    _check(load().quantize_rows(_ptr(X), rows, cols, _ld(X), _ptr(Q), Q.stride(0), _ptr(s),
+                                _stream(X)))
+    return Q, s
+
+
+def quantize_cols(X):
+    _req_matrix(X, torch.float32, "X")
+    rows, cols = X.shape
+    Qt = _int8_padded(cols, rows, X.device)
+    s = torch.empty(cols, dtype=torch.float32, device=X.device)
+    _check(load().quantize_cols(_ptr(X), rows, cols, _ld(X), _ptr(Qt), Qt.stride(0), _ptr(s),
+                                _stream(X)))
+    return Qt, s
+
+
+def workspace_bytes(M, N, K):
+    return int(load().gemm_i8_workspace_bytes(M, N, K))
+
+
+def _workspace(device, nbytes):
+    """Zero-filled workspace per (device, stream); the library leaves it
+    zeroed after every call, so it is cleared only when first allocated."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws[key] = ws
+    return ws
+
+
+def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=None):
+    _req_matrix(QA, torch.int8, "QA")
+    _req_matrix(QBt, torch.int8, "QBt")
+    M, K = QA.shape
+    N, K2 = QBt.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: QA has {K}, QBt has {K2}")
+    if s_row.dtype != torch.float32 or s_col.dtype != torch.float32:
+        raise ValueError("scales must be float32")
+    if s_row.numel() != M or s_col.numel() != N:
+        raise ValueError("scale lengths must be M and N")
+    if not (s_row.is_contiguous() and s_col.is_contiguous()):
+        raise ValueError("scales must be contiguous")
+    dev = QA.device
+    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _req_matrix(C, torch.float32, "out")
+    h = torch.zeros(1, dtype=torch.int64, device=dev) if want_hash else None
+    nbytes = workspace_bytes(M, N, K)
+    ws = _workspace(dev, nbytes)
+    flags = (I8G_RELU if relu else 0) | (I8G_HASH if want_hash else 0)
+    lda = QA.stride(0) if M > 0 else _round16(K)
+    ldb = QBt.stride(0) if N > 0 else _round16(K)
+    _check(load().gemm_i8_blockscaled(
+        _ptr(QA), lda, _ptr(s_row), _ptr(QBt), ldb, _ptr(s_col), M, N, K,
+        _ptr(C), max(C.stride(0), N, 1), flags, _ptr(h), ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), _stream(QA)))
+    return (C, h) if want_hash else C
+
+
+def output_hash(C):
+    _req_matrix(C, torch.float32, "C")
+    M, N = C.shape
+    h = torch.zeros(1, dtype=torch.int64, device=C.device)
+    ws = _workspace(C.device, 256)
+    _check(load().output_hash(_ptr(C), M, N, max(C.stride(0), N, 1), _ptr(h),
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(C)))
+    return h
+
+
+def hash_value(h) -> int:
+    """The 64-bit hash held by a 1-element int64 tensor, as an unsigned int."""
+    return int(h.item()) & ((1 << 64) - 1)
+
+
+def blockscaled_gemm(A, B, relu=False, want_hash=False):
+    """C = A @ B through the whole method: quantize_rows(A), quantize_cols(B),
+    then the int8 GEMM with its epilogue."""
+    QA, s_row = quantize_rows(A)
+    QBt, s_col = quantize_cols(B)
+    return gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=relu, want_hash=want_hash)

@@ -1,0 +1,133 @@
+// api.hip -- the C ABI of libint8_gemm.so (declared in include/int8_gemm.h):
+// argument validation, status codes, workspace layout and kernel launches
+// on the caller's stream.  No device memory is allocated here.
+#include <stdint.h>
+
+#include "../../include/int8_gemm.h"
+#include "i8g_device.h"
+#include "i8g_launch.h"
+
+using namespace i8g;
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? I8G_OK : I8G_EHIP; }
+
+int check_quantize_args(const float* X, int64_t rows, int64_t cols, int64_t ldx, const void* Q,
+                        int64_t ldq_min_ok, int64_t ldq, const float* scale) {
+  if (rows < 0 || cols < 0) return I8G_EINVAL;
+  if (rows > INT32_MAX || cols > INT32_MAX) return I8G_EINVAL;
+  if (rows == 0) return I8G_OK;
+  if (cols == 0) return scale ? I8G_OK : I8G_EINVAL;
+  if (!X || !Q || !scale) return I8G_EINVAL;
+  if (ldx < cols || ldq < ldq_min_ok) return I8G_EINVAL;
+  return I8G_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* i8g_status_string(int status) {
+  switch (status) {
+    case I8G_OK: return "ok";
+    case I8G_EINVAL: return "invalid argument (null pointer, negative size or leading dimension too small)";
+    case I8G_EKRANGE: return "K exceeds 133144: exact int32 accumulation is not guaranteed";
+    case I8G_EALIGN: return "GEMM operand not 16-byte aligned, or its leading dimension is not a multiple of 16 at least K rounded up to 16";
+    case I8G_EWORKSPACE: return "workspace missing, misaligned or smaller than gemm_i8_workspace_bytes()";
+    case I8G_EHIP: return "HIP runtime error while enqueueing a kernel";
+    default: return "unknown status";
+  }
+}
+
+const char* i8g_version(void) { return "int8_gemm 0.1.0 gfx950"; }
+
+int quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
+                  float* scale, void* stream) {
+  int st = check_quantize_args(X, rows, cols, ldx, Q, cols, ldq, scale);
+  if (st != I8G_OK || rows == 0) return st;
+  if (cols == 0 && !scale) return I8G_EINVAL;   // empty rows still get the floor scale
+  return hip_status(launch_quantize_rows(X, rows, cols, ldx, Q, ldq, scale, as_stream(stream)));
+}
+
+int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
+                  int64_t ldqt, float* scale, void* stream) {
+  int st = check_quantize_args(X, rows, cols, ldx, Qt, rows, ldqt, scale);
+  if (st != I8G_OK || cols == 0) return st;
+  if (rows == 0 && !scale) return I8G_EINVAL;   // empty columns still get the floor scale
+  return hip_status(launch_quantize_cols(X, rows, cols, ldx, Qt, ldqt, scale, as_stream(stream)));
+}
+
+size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return sizeof(WsHeader);
+  GemmPlan plan = plan_gemm(M, N, K);
+  return plan.workspace_bytes;
+}
+
+int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,
+                        int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K, float* C,
+                        int64_t ldc, uint32_t flags, uint64_t* hash, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return I8G_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX) return I8G_EINVAL;
+  if (flags & ~(I8G_RELU | I8G_HASH)) return I8G_EINVAL;
+  const bool want_hash = (flags & I8G_HASH) != 0;
+  if (want_hash && !hash) return I8G_EINVAL;
+  if (K > I8G_K_MAX) return I8G_EKRANGE;
+  if (!workspace || ((uintptr_t)workspace % 256) != 0) return I8G_EWORKSPACE;
+  if (M == 0 || N == 0) {
+    if (workspace_bytes < sizeof(WsHeader)) return I8G_EWORKSPACE;
+    if (want_hash) return hip_status(launch_output_hash(C, M, N, ldc, hash,
+                                                        reinterpret_cast<WsHeader*>(workspace),
+                                                        as_stream(stream)));
+    return I8G_OK;
+  }
+  if (!C || !s_row || !s_col || ldc < N) return I8G_EINVAL;
+  if (K > 0 && (!QA || !QBt)) return I8G_EINVAL;
+  const int64_t k16 = (K + 15) / 16 * 16;
+  if (K > 0) {
+    if (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < k16 ||
+        ldb < k16)
+      return I8G_EALIGN;
+  }
+  GemmPlan plan = plan_gemm(M, N, K > 0 ? K : 1);
+  if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
+  GemmParams p;
+  p.A = QA;
+  p.B = QBt;
+  p.s_row = s_row;
+  p.s_col = s_col;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = plan.tiles_m;
+  p.tiles_n = plan.tiles_n;
+  p.splits = plan.splits;
+  p.k_per_split = plan.k_per_split;
+  p.relu = (flags & I8G_RELU) ? 1 : 0;
+  p.do_hash = want_hash ? 1 : 0;
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.ws = reinterpret_cast<WsHeader*>(ws);
+  p.tickets = reinterpret_cast<unsigned int*>(ws + plan.tickets_offset);
+  p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
+  p.hash_out = hash;
+  return hip_status(launch_gemm(p, plan, as_stream(stream)));
+}
+
+int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* hash, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || !hash) return I8G_EINVAL;
+  if (M > 0 && N > 0 && (!C || ldc < N)) return I8G_EINVAL;
+  if (!workspace || ((uintptr_t)workspace % 256) != 0 || workspace_bytes < sizeof(WsHeader))
+    return I8G_EWORKSPACE;
+  return hip_status(launch_output_hash(C, M, N, ldc, hash, reinterpret_cast<WsHeader*>(workspace),
+                                       as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// i8g_device.h -- device-side arithmetic shared by the library's kernels.
+//
+// Every float operation of the method is written here once, as a separate
+// IEEE binary32 operation rounded to nearest-even.  The library is compiled
+// with -ffp-contract=off and the helpers carry `#pragma clang fp
+// contract(off)`, so no multiply is ever fused with the following add (the
+// DaisyChain-Train page "Verification -- why you can trust the numbers",
+// section "The verified INT8 units", step 3 rounds after each multiply; its
+// section "Hardware ground truth (RDNA2 ISA audit)" discusses the fused
+// quantizer, which gives different int8 next to |x*inv| = 0.5).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8g {
+
+// RN(1e-8): the scale floor of step 1, bit pattern 0x322BCC77.
+__device__ __forceinline__ float scale_floor() { return __uint_as_float(0x322BCC77u); }
+
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
+__device__ __forceinline__ float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+// Correctly rounded division: the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt, which makes '/' the IEEE
+// division (never the approximate reciprocal instruction).
+__device__ __forceinline__ float div_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a / b;
+}
+
+// Step 1: s = max(RN(a/127), RN(1e-8)).  a >= 0 and finite, so the larger
+// of the two is well defined; fmaxf on two non-NaN, non-zero-tie values is
+// exact.
+__device__ __forceinline__ float scale_of_absmax(float a) {
+  float s = div_rn(a, 127.0f);
+  float f = scale_floor();
+  return s > f ? s : f;
+}
+
+__device__ __forceinline__ float recip_rn(float s) { return div_rn(1.0f, s); }
+
+// q = floor(RN(RN(x*inv) + 0.5)), in [-127, 127] for |x| <= the line max.
+__device__ __forceinline__ int quantize1(float x, float inv) {
+  float t = mul_rn(x, inv);
+  float u = add_rn(t, 0.5f);
+  return (int)floorf(u);
+}
+
+// Step 3: out = RN(RN(RN(acc)*s_row)*s_col); int->float conversion rounds
+// to nearest-even (the MODE register's default, which HIP kernels run with).
+__device__ __forceinline__ float epilogue1(int acc, float s_row, float s_col) {
+  float y = (float)acc;
+  y = mul_rn(y, s_row);
+  return mul_rn(y, s_col);
+}
+
+// ReLU that never produces -0: out > 0 ? out : +0.
+__device__ __forceinline__ float relu_pos0(float y) { return y > 0.0f ? y : 0.0f; }
+
+// ---------------------------------------------------------------------------
+// Output hash (see include/int8_gemm.h, output_hash):
+//   S = sum_{i,j} c(j) * r(i) * bits(i,j) mod 2^64,
+//   H = fmix64(S ^ fmix64(M*2^32 + N)).
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ uint64_t fmix64(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xFF51AFD7ED558CCDull;
+  k ^= k >> 33;
+  k *= 0xC4CEB9FE1A85EC53ull;
+  k ^= k >> 33;
+  return k;
+}
+
+__host__ __device__ __forceinline__ uint32_t mix31(uint32_t x) {
+  const uint32_t m = 0x7FFFFFFFu;
+  x &= m;
+  x ^= x >> 16;
+  x = (x * 0x3B9C5A1Du) & m;
+  x ^= x >> 13;
+  x = (x * 0x2F6E8B35u) & m;
+  x ^= x >> 16;
+  return x;
+}
+
+__host__ __device__ __forceinline__ uint32_t hash_row_key(uint32_t i) { return (mix31(i) << 1) | 1u; }
+
+__host__ __device__ __forceinline__ uint64_t hash_col_key(uint64_t j) {
+  return fmix64(j + 0x9E3779B97F4A7C15ull) | 1ull;
+}
+
+__host__ __device__ __forceinline__ uint64_t hash_finalize(uint64_t s, uint64_t m, uint64_t n) {
+  return fmix64(s ^ fmix64((m << 32) | n));
+}
+
+// Sum of a 64-bit value over the 64 lanes of a wavefront (mod 2^64).
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Workspace header shared by the GEMM and the hash kernels.  It must start
+// zeroed; the last workgroup of a call returns it to zero.
+struct WsHeader {
+  unsigned long long hash_sum;   // S, accumulated with device-scope atomics
+  unsigned int done;             // workgroups that have added their part of S
+  unsigned int pad[61];          // keeps the header 256 bytes
+};
+static_assert(sizeof(WsHeader) == 256, "workspace header must be 256 bytes");
+
+// Adds this workgroup's part of S, and lets the last workgroup of the grid
+// write H and reset the header.  Call from every thread of the workgroup
+// after `part` holds the workgroup total in thread 0 (other threads pass 0).
+// `red` is LDS scratch of at least one uint32.
+__device__ __forceinline__ void hash_commit(WsHeader* ws, uint64_t part, unsigned int n_groups,
+                                            uint64_t M, uint64_t N, uint64_t* hash_out,
+                                            unsigned int* red) {
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&ws->hash_sum, (unsigned long long)part, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    unsigned int t = __hip_atomic_fetch_add(&ws->done, 1u, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    if (t == n_groups - 1) {
+      unsigned long long s = __hip_atomic_exchange(&ws->hash_sum, 0ull, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ws->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *hash_out = hash_finalize(s, M, N);
+    }
+  }
+  (void)red;
+}
+
+}  // namespace i8g

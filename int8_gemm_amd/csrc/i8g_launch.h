@@ -1,0 +1,49 @@
+// i8g_launch.h -- host-side interface between the C ABI (api.hip) and the
+// kernels (quantize.hip, gemm.hip, hash.hip).  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace i8g {
+
+struct WsHeader;
+
+struct GemmParams {
+  const int8_t* A;          // QA, M x K, K contiguous
+  const int8_t* B;          // QBt, N x K, K contiguous
+  const float* s_row;
+  const float* s_col;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  int tiles_m, tiles_n, splits, k_per_split;
+  int relu, do_hash;
+  WsHeader* ws;
+  unsigned int* tickets;
+  int* partials;
+  uint64_t* hash_out;
+};
+
+struct GemmPlan {
+  int cfg;                  // index of the tile configuration
+  int bm, bn;
+  int tiles_m, tiles_n;
+  int splits;
+  int k_per_split;          // bytes of K per split (multiple of 64)
+  size_t tickets_offset;
+  size_t partials_offset;
+  size_t workspace_bytes;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
+
+hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                int8_t* Q, int64_t ldq, float* scale, hipStream_t stream);
+hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream);
+hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
+                              uint64_t* hash, WsHeader* ws, hipStream_t stream);
+
+}  // namespace i8g

@@ -1,0 +1,299 @@
+// quantize.hip -- per-row and per-column absmax quantization to int8.
+//
+// Step 1 of the DaisyChain-Train page "Verification -- why you can trust
+// the numbers", section "The verified INT8 units": scale = max(|line|)/127
+// floored at 1e-8, values to int8; with the readings of this library
+// (include/int8_gemm.h): s = max(RN(a/127), RN(1e-8)), inv = RN(1/s),
+// q = floor(RN(RN(x*inv) + 0.5)).
+//
+// Both passes are HBM-bound (4 bytes read + 1 byte written per element).
+//  * rows: one wavefront per row for rows up to 4096 elements, the row held
+//    in registers between the absmax and the quantize (one HBM read); a
+//    1024-thread workgroup per row beyond that (registers up to 65536
+//    elements, a second read from cache above).  The row max is a wave
+//    butterfly reduction (plus LDS across waves).
+//  * cols: the column max needs every row first, so it is a grid-wide
+//    reduction: zero the scale array, a column-max kernel combines
+//    workgroup maxima with atomicMax on the bit patterns of |x| (for
+//    non-negative floats the integer order is the float order, so the
+//    result is exact and order-free), then a quantize kernel transposes
+//    64x64 tiles through LDS into the K-contiguous int8 output, and a last
+//    kernel turns the stored maxima into scales.
+#include "i8g_device.h"
+#include "i8g_launch.h"
+
+namespace i8g {
+
+// Four consecutive elements of a row starting at column c (c % 4 == 0),
+// zero beyond `cols`.  `vec` selects one 16-byte load (row base aligned).
+__device__ __forceinline__ float4 load4(const float* row, int64_t c, int64_t cols, bool vec) {
+  if (vec && c + 4 <= cols) return *reinterpret_cast<const float4*>(row + c);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < cols) v.x = row[c];
+  if (c + 1 < cols) v.y = row[c + 1];
+  if (c + 2 < cols) v.z = row[c + 2];
+  if (c + 3 < cols) v.w = row[c + 3];
+  return v;
+}
+
+__device__ __forceinline__ float absmax4(float m, float4 v) {
+  m = fmaxf(m, fabsf(v.x));
+  m = fmaxf(m, fabsf(v.y));
+  m = fmaxf(m, fabsf(v.z));
+  return fmaxf(m, fabsf(v.w));
+}
+
+__device__ __forceinline__ unsigned int pack4(float4 v, float inv) {
+  unsigned int b0 = (unsigned int)(quantize1(v.x, inv) & 0xFF);
+  unsigned int b1 = (unsigned int)(quantize1(v.y, inv) & 0xFF);
+  unsigned int b2 = (unsigned int)(quantize1(v.z, inv) & 0xFF);
+  unsigned int b3 = (unsigned int)(quantize1(v.w, inv) & 0xFF);
+  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+__device__ __forceinline__ void store4(int8_t* row, int64_t c, int64_t cols, unsigned int q,
+                                       bool vec) {
+  if (vec && c + 4 <= cols) {
+    *reinterpret_cast<unsigned int*>(row + c) = q;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (c + e < cols) row[c + e] = (int8_t)((q >> (8 * e)) & 0xFF);
+}
+
+// ---------------------------------------------------------------------------
+// rows: one wavefront per row, VPL groups of 4 elements per lane in registers
+// ---------------------------------------------------------------------------
+template <int VPL>
+__global__ void __launch_bounds__(256)
+qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                  int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
+                  int vec_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* xr = X + r * ldx;
+  float4 v[VPL];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    v[i] = load4(xr, (int64_t)(lane + 64 * i) * 4, cols, vec_in);
+    m = absmax4(m, v[i]);
+  }
+  m = wave_max_f32(m);
+  const float s = scale_of_absmax(m);
+  const float inv = recip_rn(s);
+  if (lane == 0) scale[r] = s;
+  int8_t* qr = Q + r * ldq;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int64_t c = (int64_t)(lane + 64 * i) * 4;
+    if (c < cols) store4(qr, c, cols, pack4(v[i], inv), vec_out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rows: one 1024-thread workgroup per row (long rows)
+// ---------------------------------------------------------------------------
+template <int VPT>
+__global__ void __launch_bounds__(1024)
+qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                   int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
+                   int vec_out) {
+  constexpr int NT = 1024;
+  constexpr int64_t CHUNK = (int64_t)NT * VPT * 4;
+  __shared__ float red[NT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* xr = X + r * ldx;
+  int8_t* qr = Q + r * ldq;
+  float4 v[VPT];
+  float m = 0.0f;
+  for (int64_t base = 0; base < cols; base += CHUNK) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      v[i] = load4(xr, base + (int64_t)(tid + NT * i) * 4, cols, vec_in);
+      m = absmax4(m, v[i]);
+    }
+  }
+  m = wave_max_f32(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (wave == 0) {
+    float w = lane < NT / 64 ? red[lane] : 0.0f;
+    w = wave_max_f32(w);
+    if (lane == 0) red[0] = w;
+  }
+  __syncthreads();
+  const float s = scale_of_absmax(red[0]);
+  const float inv = recip_rn(s);
+  if (tid == 0) scale[r] = s;
+  if (cols <= CHUNK) {   // the row is still in registers
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t c = (int64_t)(tid + NT * i) * 4;
+      if (c < cols) store4(qr, c, cols, pack4(v[i], inv), vec_out);
+    }
+  } else {               // reread (from L2 / MALL)
+    for (int64_t base = 0; base < cols; base += CHUNK) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int64_t c = base + (int64_t)(tid + NT * i) * 4;
+        if (c < cols) store4(qr, c, cols, pack4(load4(xr, c, cols, vec_in), inv), vec_out);
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                int8_t* Q, int64_t ldq, float* scale, hipStream_t stream) {
+  const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
+  const int vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
+  if (cols <= 256 * 16) {
+    const dim3 grid((unsigned int)((rows + 3) / 4)), block(256);
+    if (cols <= 256)
+      hipLaunchKernelGGL(qrows_wave_kernel<1>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else if (cols <= 512)
+      hipLaunchKernelGGL(qrows_wave_kernel<2>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else if (cols <= 768)
+      hipLaunchKernelGGL(qrows_wave_kernel<3>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else if (cols <= 1024)
+      hipLaunchKernelGGL(qrows_wave_kernel<4>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else if (cols <= 2048)
+      hipLaunchKernelGGL(qrows_wave_kernel<8>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else if (cols <= 3072)
+      hipLaunchKernelGGL(qrows_wave_kernel<12>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else
+      hipLaunchKernelGGL(qrows_wave_kernel<16>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+  } else {
+    const dim3 grid((unsigned int)rows), block(1024);
+    if (cols <= 1024 * 8 * 4)
+      hipLaunchKernelGGL(qrows_block_kernel<8>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+    else
+      hipLaunchKernelGGL(qrows_block_kernel<16>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// cols
+// ---------------------------------------------------------------------------
+__global__ void fill_zero_u32_kernel(unsigned int* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Column maxima of a ROWS_PER_WG x 256 block; combined across workgroups
+// with atomicMax on the bit patterns of |x| (stored in `maxbits`).
+constexpr int QC_ROWS = 64;
+
+__global__ void __launch_bounds__(256)
+qcols_max_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                 unsigned int* __restrict__ maxbits, int vec_in) {
+  __shared__ float red[4][256];
+  const int tid = threadIdx.x;
+  const int cg = tid & 63, ph = tid >> 6;          // column group of 4, row phase
+  const int64_t c = (int64_t)blockIdx.x * 256 + cg * 4;
+  const int64_t r0 = (int64_t)blockIdx.y * QC_ROWS;
+  int64_t r1 = r0 + QC_ROWS;
+  if (r1 > rows) r1 = rows;
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < cols) {
+    for (int64_t r = r0 + ph; r < r1; r += 4) {
+      float4 v = load4(X + r * ldx, c, cols, vec_in);
+      m.x = fmaxf(m.x, fabsf(v.x));
+      m.y = fmaxf(m.y, fabsf(v.y));
+      m.z = fmaxf(m.z, fabsf(v.z));
+      m.w = fmaxf(m.w, fabsf(v.w));
+    }
+  }
+  red[ph][cg * 4 + 0] = m.x;
+  red[ph][cg * 4 + 1] = m.y;
+  red[ph][cg * 4 + 2] = m.z;
+  red[ph][cg * 4 + 3] = m.w;
+  __syncthreads();
+  const float t = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+  const int64_t col = (int64_t)blockIdx.x * 256 + tid;
+  if (col < cols) atomicMax(maxbits + col, __float_as_uint(t));
+}
+
+// Quantize a 64 (rows of X = k) x 64 (columns of X = j) tile with the column
+// scales, transpose through LDS, write 64 rows of Qt (64 bytes each).
+__global__ void __launch_bounds__(256)
+qcols_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                   int8_t* __restrict__ Qt, int64_t ldqt, const unsigned int* __restrict__ maxbits,
+                   int vec_in, int vec_out) {
+  __shared__ float s_inv[64];
+  __shared__ unsigned int tq[64][17];              // [j][k/4], padded
+  const int tid = threadIdx.x;
+  const int64_t j0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
+  if (tid < 64) {
+    const int64_t j = j0 + tid;
+    const float a = j < cols ? __uint_as_float(maxbits[j]) : 0.0f;
+    s_inv[tid] = recip_rn(scale_of_absmax(a));
+  }
+  __syncthreads();
+  const int cg = tid & 15, rr = tid >> 4;          // 16 groups of 4 columns, 16 rows
+  const float i0 = s_inv[cg * 4], i1 = s_inv[cg * 4 + 1], i2 = s_inv[cg * 4 + 2], i3 = s_inv[cg * 4 + 3];
+  // each thread quantizes rows k = 4*rr .. 4*rr+3 of its 4 columns, so it can
+  // pack 4 consecutive k of one column into one 32-bit word of tq.
+  unsigned int w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t k = k0 + rr * 4 + e;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < rows) v = load4(X + k * ldx, j0 + cg * 4, cols, vec_in);
+    w0 |= (unsigned int)(quantize1(v.x, i0) & 0xFF) << (8 * e);
+    w1 |= (unsigned int)(quantize1(v.y, i1) & 0xFF) << (8 * e);
+    w2 |= (unsigned int)(quantize1(v.z, i2) & 0xFF) << (8 * e);
+    w3 |= (unsigned int)(quantize1(v.w, i3) & 0xFF) << (8 * e);
+  }
+  tq[cg * 4 + 0][rr] = w0;
+  tq[cg * 4 + 1][rr] = w1;
+  tq[cg * 4 + 2][rr] = w2;
+  tq[cg * 4 + 3][rr] = w3;
+  __syncthreads();
+  // write: thread -> (row jl = tid/4 of Qt, 16-byte chunk tid%4)
+  const int jl = tid >> 2, ch = tid & 3;
+  const int64_t j = j0 + jl;
+  if (j >= cols) return;
+  int8_t* dst = Qt + j * ldqt;
+  const int64_t k = k0 + ch * 16;
+  if (k >= rows) return;
+  const unsigned int a = tq[jl][ch * 4], b = tq[jl][ch * 4 + 1], c = tq[jl][ch * 4 + 2],
+                     d = tq[jl][ch * 4 + 3];
+  if (vec_out && k + 16 <= rows) {
+    *reinterpret_cast<uint4*>(dst + k) = make_uint4(a, b, c, d);
+  } else {
+    const unsigned int w[4] = {a, b, c, d};
+    for (int e = 0; e < 16 && k + e < rows; ++e) dst[k + e] = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
+  }
+}
+
+__global__ void qcols_scale_kernel(float* scale, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) scale[i] = scale_of_absmax(scale[i]);   // scale[i] holds the column max
+}
+
+hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream) {
+  const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
+  const int vec_out = ((uintptr_t)Qt % 16 == 0) && (ldqt % 16 == 0);
+  unsigned int* maxbits = reinterpret_cast<unsigned int*>(scale);
+  hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
+                     stream, maxbits, cols);
+  if (rows > 0) {
+  hipLaunchKernelGGL(qcols_max_kernel,
+                     dim3((unsigned int)((cols + 255) / 256), (unsigned int)((rows + QC_ROWS - 1) / QC_ROWS)),
+                     dim3(256), 0, stream, X, rows, cols, ldx, maxbits, vec_in);
+  hipLaunchKernelGGL(qcols_quant_kernel,
+                     dim3((unsigned int)((cols + 63) / 64), (unsigned int)((rows + 63) / 64)), dim3(256), 0,
+                     stream, X, rows, cols, ldx, Qt, ldqt, (const unsigned int*)maxbits, vec_in, vec_out);
+  }
+  hipLaunchKernelGGL(qcols_scale_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
+                     stream, scale, cols);
+  return hipGetLastError();
+}
+
+}  // namespace i8g

@@ -1,0 +1,46 @@
+"""The C-ABI library loads on a host without a GPU and exports every symbol
+that include/int8_gemm.h declares (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+
+def _declared(repo_root):
+    text = open(os.path.join(repo_root, "include", "int8_gemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text)
+    return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
+
+
+def test_header_declares_the_four_entry_points(repo_root):
+    names = _declared(repo_root)
+    for n in ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "output_hash"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(repo_root):
+    import int8_gemm_amd as g
+    if not os.path.exists(g.library_path()):
+        pytest.fail("libint8_gemm.so is not built (python -m int8_gemm_amd.build)")
+    lib = g.load()
+    for n in _declared(repo_root):
+        assert hasattr(lib, n), n
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr)
+    assert set(g.EXPORTED) == set(_declared(repo_root))
+
+
+def test_host_only_calls(repo_root):
+    """Calls that touch no device: status strings, version, workspace sizing."""
+    import int8_gemm_amd as g
+    lib = g.load()
+    assert lib.i8g_version().startswith(b"int8_gemm")
+    for st in range(6):
+        assert lib.i8g_status_string(st)
+    assert lib.i8g_status_string(99) == b"unknown status"
+    assert g.workspace_bytes(256, 256, 256) >= 256
+    assert g.workspace_bytes(0, 5, 5) == 256
+    # argument errors are reported before anything is enqueued
+    assert lib.quantize_rows(None, -1, 2, 2, None, 2, None, None) == 1
+    assert lib.output_hash(None, 1, 1, 1, None, None, 0, None) == 1

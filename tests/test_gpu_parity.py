@@ -1,0 +1,314 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+The bar is bit-exact: int8 bytes, scale bit patterns, output bit patterns
+(so -0 and +0 differ) and the 64-bit output hash.  The DaisyChain-Train page
+"Verification — why you can trust the numbers" compares "at the bit level"
+in its init gates ("Layer 1: exact init gates") for exactly this reason.
+
+Every case prints its name before it touches the GPU.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import adversarial, hashref, ref
+from synth import inputs as S
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+U32 = np.uint32
+
+
+@pytest.fixture(scope="module")
+def g():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import int8_gemm_amd as lib
+    lib.load()
+    return lib
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run_method(g, A, B, relu, want_hash=True):
+    """The whole method on the GPU; returns numpy copies of every stage."""
+    QA, sr = g.quantize_rows(to_dev(A))
+    QBt, sc = g.quantize_cols(to_dev(B))
+    C, h = g.gemm_i8_blockscaled(QA, sr, QBt, sc, relu=relu, want_hash=True)
+    torch.cuda.synchronize()
+    return dict(QA=QA.cpu().numpy(), s_row=sr.cpu().numpy(), QBt=QBt.cpu().numpy(),
+                s_col=sc.cpu().numpy(), C=C.cpu().numpy(), hash=g.hash_value(h))
+
+
+def assert_bits(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if got.dtype == np.float32:
+        bad = got.view(U32) != want.view(U32)
+    else:
+        bad = got != want
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = [(tuple(i), got[tuple(i)], want[tuple(i)]) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} differ, e.g. {detail}")
+
+
+def check_against_oracle(got, A, B, relu):
+    C, QA, s_row, QBt, s_col = ref.blockscaled_gemm(A, B, relu)
+    assert_bits(got["QA"], QA, "QA")
+    assert_bits(got["s_row"], s_row, "s_row")
+    assert_bits(got["QBt"], QBt, "QBt")
+    assert_bits(got["s_col"], s_col, "s_col")
+    assert_bits(got["C"], C, "C")
+    assert got["hash"] == hashref.output_hash(C), "hash"
+    return C
+
+
+def adversarial_inputs(c):
+    case = S.adversarial_case(c)
+    rng = np.random.default_rng([7, c])
+    A, _ = adversarial.plant_ties(case.A, "rows", rng, frac=0.02)
+    A, _ = adversarial.plant_fma_splits(A, "rows", rng, per_line=1)
+    B, _ = adversarial.plant_ties(case.B, "cols", rng, frac=0.02)
+    B, _ = adversarial.plant_fma_splits(B, "cols", rng, per_line=1)
+    return A, B, case.relu
+
+
+# ---------------------------------------------------------------------------
+# quantize
+# ---------------------------------------------------------------------------
+QR_SHAPES = [(1, 1), (3, 5), (17, 300), (64, 768), (100, 1000), (9, 3072), (7, 4097),
+             (3, 5000), (2, 33000), (2, 70000)]
+
+
+def _quant_input(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_t(2, (rows, cols)).astype(F32)
+    X[rng.random((rows, cols)) < 0.01] = F32(-0.0)
+    if rows > 2:
+        X[1] = 0
+    X, _ = adversarial.plant_ties(X, "rows", rng, frac=0.02)
+    X, _ = adversarial.plant_fma_splits(X, "rows", rng, per_line=2)
+    return X
+
+
+@pytest.mark.parametrize("rows,cols", QR_SHAPES)
+def test_quantize_rows_parity(g, rows, cols):
+    say("quantize_rows", rows, cols)
+    X = _quant_input(rows, cols, rows * 100003 + cols)
+    Q, s = g.quantize_rows(to_dev(X))
+    Qo, so = ref.quantize_rows(X)
+    assert_bits(Q.cpu().numpy(), Qo, "Q")
+    assert_bits(s.cpu().numpy(), so, "scale")
+
+
+def test_quantize_rows_unaligned(g):
+    say("quantize_rows unaligned view")
+    base = _quant_input(33, 771, 5)
+    dev = to_dev(base)[:, 1:]            # pointer and ld not multiples of 4 floats
+    Q, s = g.quantize_rows(dev)
+    Qo, so = ref.quantize_rows(base[:, 1:])
+    assert_bits(Q.cpu().numpy(), Qo, "Q")
+    assert_bits(s.cpu().numpy(), so, "scale")
+
+
+QC_SHAPES = [(1, 1), (5, 3), (300, 17), (768, 64), (1000, 100), (130, 257), (3072, 40), (65, 1030)]
+
+
+@pytest.mark.parametrize("rows,cols", QC_SHAPES)
+def test_quantize_cols_parity(g, rows, cols):
+    say("quantize_cols", rows, cols)
+    X = np.ascontiguousarray(_quant_input(cols, rows, rows * 7919 + cols).T)
+    Qt, s = g.quantize_cols(to_dev(X))
+    Qo, so = ref.quantize_cols(X)
+    assert_bits(Qt.cpu().numpy(), Qo, "Qt")
+    assert_bits(s.cpu().numpy(), so, "scale")
+
+
+def test_quantize_cols_unaligned(g):
+    say("quantize_cols unaligned view")
+    base = np.ascontiguousarray(_quant_input(130, 67, 6).T)      # 67 x 130
+    dev = to_dev(base)[:, 3:]
+    Qt, s = g.quantize_cols(dev)
+    Qo, so = ref.quantize_cols(base[:, 3:])
+    assert_bits(Qt.cpu().numpy(), Qo, "Qt")
+    assert_bits(s.cpu().numpy(), so, "scale")
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+def test_w1_single_gemm_256(g):
+    say("w1 256x256x256")
+    A, B = S.w1_inputs()
+    got = run_method(g, A, B, relu=False)
+    check_against_oracle(got, A, B, relu=False)
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_w4_adversarial_sweep(g, chunk):
+    for c in range(chunk * 50, (chunk + 1) * 50):
+        A, B, relu = adversarial_inputs(c)
+        say("w4 case", c, "MNK", A.shape[0], B.shape[1], A.shape[1], "relu", relu)
+        got = run_method(g, A, B, relu)
+        C = check_against_oracle(got, A, B, relu)
+        if relu:
+            assert np.all(got["C"].view(U32) >> 31 == 0)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_tile_and_split_invariance(g, tile):
+    """Different tile shapes and K splits give byte-identical outputs (integer
+    accumulation is associative), all equal to the oracle."""
+    rng = np.random.default_rng(77)
+    A = rng.standard_t(3, (300, 3000)).astype(F32)
+    B = rng.standard_normal((3000, 520)).astype(F32)
+    C, *_ = ref.blockscaled_gemm(A, B, True)
+    h = hashref.output_hash(C)
+    try:
+        for splits in (1, 2, 5, 16):
+            os.environ["I8G_FORCE_TILE"] = str(tile)
+            os.environ["I8G_FORCE_SPLITS"] = str(splits)
+            say("invariance tile", tile, "splits", splits)
+            got = run_method(g, A, B, relu=True)
+            assert_bits(got["C"], C, f"C tile {tile} splits {splits}")
+            assert got["hash"] == h
+    finally:
+        os.environ.pop("I8G_FORCE_TILE", None)
+        os.environ.pop("I8G_FORCE_SPLITS", None)
+
+
+def test_w2_mlp_full_size(g):
+    """MLP up-projection (ReLU) and the down-projection on its output, full
+    size, every output byte."""
+    X, W_up, W_down = S.w2_inputs()
+    say("w2 up 8192x3072x768 relu")
+    got = run_method(g, X, W_up, relu=True)
+    H = check_against_oracle(got, X, W_up, relu=True)
+    say("w2 down 8192x768x3072")
+    got2 = run_method(g, got["C"], W_down, relu=False)
+    check_against_oracle(got2, H, W_down, relu=False)
+
+
+def test_long_k_split(g):
+    """A long-K shape that the planner splits (the LM-head dgrad's K=50304,
+    at reduced M and N), every byte."""
+    rng = np.random.default_rng(78)
+    A = (rng.standard_normal((512, 50304)) * 1e-4).astype(F32)
+    B = (rng.standard_normal((50304, 256)) * 0.02).astype(F32)
+    say("long K 512x256x50304")
+    got = run_method(g, A, B, relu=False)
+    check_against_oracle(got, A, B, relu=False)
+
+
+# ---------------------------------------------------------------------------
+# hash, errors, workspace
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,pad", [(1, 1, 0), (3, 5, 0), (37, 1029, 3), (513, 64, 0), (5, 4, 0)])
+def test_output_hash_parity(g, m, n, pad):
+    say("output_hash", m, n, pad)
+    rng = np.random.default_rng(m * 31 + n)
+    base = rng.standard_normal((m, n + pad)).astype(F32)
+    base[rng.random(base.shape) < 0.1] = F32(-0.0)
+    dev = to_dev(base)[:, :n]
+    h = g.hash_value(g.output_hash(dev))
+    assert h == hashref.output_hash(np.ascontiguousarray(base[:, :n]))
+
+
+def test_empty_shapes(g):
+    say("empty shapes")
+    z = torch.zeros((0, 5), dtype=torch.float32, device="cuda")
+    assert g.hash_value(g.output_hash(z)) == hashref.output_hash(np.zeros((0, 5), F32))
+    Q, s = g.quantize_rows(z)
+    assert Q.shape == (0, 5) and s.shape == (0,)
+    A = torch.zeros((4, 0), dtype=torch.float32, device="cuda")
+    QA, sr = g.quantize_rows(A)
+    assert np.all(sr.cpu().numpy().view(U32) == 0x322BCC77)
+    QB, sc = g.quantize_cols(torch.zeros((0, 3), dtype=torch.float32, device="cuda"))
+    C, h = g.gemm_i8_blockscaled(QA, sr, QB, sc, want_hash=True)
+    torch.cuda.synchronize()
+    assert np.all(C.cpu().numpy().view(U32) == 0)
+    assert g.hash_value(h) == hashref.output_hash(np.zeros((4, 3), F32))
+
+
+def test_error_statuses(g):
+    say("error statuses")
+    QA = torch.zeros((2, ref.K_MAX + 1), dtype=torch.int8, device="cuda")
+    s = torch.ones(2, dtype=torch.float32, device="cuda")
+    with pytest.raises(g.I8GError) as e:
+        g.gemm_i8_blockscaled(QA, s, QA, s)
+    assert e.value.status == 2
+    QA = torch.zeros((2, 48), dtype=torch.int8, device="cuda")[:, 1:33]   # misaligned
+    with pytest.raises(g.I8GError) as e:
+        g.gemm_i8_blockscaled(QA, s, QA, s)
+    assert e.value.status == 3
+    lib = g.load()
+    rc = lib.gemm_i8_blockscaled(None, 16, None, None, 16, None, 2, 2, 16, None, 2, 0, None,
+                                 None, 0, None)
+    assert rc == 4                                   # no workspace
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    rc = lib.gemm_i8_blockscaled(None, 16, None, None, 16, None, 2, 2, 16, None, 2, 0, None,
+                                 ws.data_ptr(), 256, None)
+    assert rc == 1                                   # null operands
+    rc = lib.quantize_rows(None, -1, 2, 2, None, 2, None, None)
+    assert rc == 1
+
+
+def test_workspace_control_words_reset(g):
+    """The workspace header returns to zero after each call, and the same
+    workspace serves repeated split-K calls (tickets reset), with identical
+    bytes each time."""
+    say("workspace control words")
+    rng = np.random.default_rng(79)
+    A = rng.standard_normal((700, 9000)).astype(F32)
+    B = rng.standard_normal((9000, 300)).astype(F32)
+    first = run_method(g, A, B, relu=False)
+    for ws in g._ws.values():
+        assert int(torch.count_nonzero(ws[:256]).item()) == 0
+    for _ in range(3):
+        again = run_method(g, A, B, relu=False)
+        assert_bits(again["C"], first["C"], "repeat")
+        assert again["hash"] == first["hash"]
+    C, *_ = ref.blockscaled_gemm(A, B, False)
+    assert_bits(first["C"], C, "C")
+
+
+def test_metamorphic_on_gpu(g):
+    """Section "Layer 5" relations and absolutes, checked on the GPU output."""
+    rng = np.random.default_rng(80)
+    A = rng.standard_t(2, (333, 555)).astype(F32)
+    B = rng.standard_t(2, (555, 444)).astype(F32)
+    say("metamorphic base")
+    C = run_method(g, A, B, relu=False)["C"]
+    p = rng.permutation(333)
+    say("metamorphic permuted rows")
+    Cp = run_method(g, A[p], B, relu=False)["C"]
+    assert_bits(Cp, C[p], "row permutation")
+    A0 = A.copy(); A0[10] = 0
+    say("metamorphic zero row")
+    C0 = run_method(g, A0, B, relu=False)["C"]
+    assert np.all(C0[10].view(U32) == 0)
+    say("metamorphic blocks")
+    top = run_method(g, A[:100], B, relu=False)["C"]
+    assert_bits(top, C[:100], "row block")
+    right = run_method(g, A, B[:, 200:], relu=False)["C"]
+    assert_bits(right, C[:, 200:], "column block")
+    say("metamorphic relu")
+    Cr = run_method(g, A, B, relu=True)["C"]
+    assert np.all(Cr.view(U32) >> 31 == 0)
+    assert np.array_equal(Cr, np.where(C > 0, C, 0))
+    # unit scales: integer inputs whose lines contain +-127 give the exact dot product
+    Ai = rng.integers(-127, 128, (64, 1000)).astype(F32); Ai[:, 0] = 127
+    Bi = rng.integers(-127, 128, (1000, 48)).astype(F32); Bi[0, :] = -127
+    say("unit scales")
+    Ci = run_method(g, Ai, Bi, relu=False)["C"]
+    exact = Ai.astype(np.int64) @ Bi.astype(np.int64)
+    assert np.array_equal(Ci.astype(np.int64), exact)
