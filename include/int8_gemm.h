@@ -42,6 +42,8 @@
  *     the hash of an empty output where one is requested.
  *   - The library allocates no device memory.  Calls that share a
  *     workspace must be ordered (same stream, or synchronized).
+ *   - No kernel waits on another workgroup and no call synchronizes with
+ *     the host.
  */
 #ifndef INT8_GEMM_H
 #define INT8_GEMM_H
@@ -59,7 +61,7 @@ extern "C" {
 #define I8G_EKRANGE     2  /* K > 133144: int32 accumulation could overflow  */
 #define I8G_EALIGN      3  /* a GEMM operand's pointer or ld not 16-byte     */
                            /* aligned, or ld below K rounded up to 16        */
-#define I8G_EWORKSPACE  4  /* workspace missing or smaller than required     */
+#define I8G_EWORKSPACE  4  /* workspace missing, misaligned or too small     */
 #define I8G_EHIP        5  /* the HIP runtime reported a launch error        */
 
 /* flags of gemm_i8_blockscaled */
@@ -114,11 +116,9 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
  *          ignored): receives output_hash(C) for this output.
  *   workspace, workspace_bytes
  *          device scratch of at least gemm_i8_workspace_bytes(M, N, K)
- *          bytes, 256-byte aligned.  It must be zero-filled before its
- *          first use.  Every call that completes returns its control words
- *          (the 256-byte header and the per-tile tickets after it) to zero,
- *          so one zeroed buffer serves any sequence of ordered calls; the
- *          rest is scratch (int32 partial tiles) with unspecified contents.
+ *          bytes, 256-byte aligned, with any contents (nothing needs to be
+ *          initialized; the call overwrites what it uses: per-tile shares
+ *          of the hash and, when K is split, int32 partial sums).
  * acc[i,j] = sum_k QA[i,k]*QBt[j,k] is exact (int32); the K range may be
  * split across workgroups, which cannot change a byte since integer
  * addition is associative.
@@ -138,6 +138,9 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row,
 /* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256). */
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* Bytes of workspace output_hash needs (a constant, 16 KiB). */
+size_t output_hash_workspace_bytes(void);
+
 /*
  * output_hash -- the probe hash of an M x N f32 matrix (the page's "Layer
  * 3: the kernel probe"; the page names no function, this library defines):
@@ -150,8 +153,10 @@ size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   H         = fmix64(S ^ fmix64(M * 2^32 + N))
  *   C      M x N f32, leading dimension ldc >= N; M, N < 2^31.
  *   hash   device pointer to one uint64_t that receives H.
- *   workspace  as for gemm_i8_blockscaled (any buffer of >= 256 zeroed
- *          bytes; left zeroed).
+ *   workspace  device scratch of output_hash_workspace_bytes() bytes,
+ *          256-byte aligned, any contents.
+ * The sum is taken modulo 2^64, so it is reduced in any order (per-
+ * workgroup shares, then one add-up), with no atomics.
  * Errors: I8G_EINVAL, I8G_EWORKSPACE, I8G_EHIP.
  */
 int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,

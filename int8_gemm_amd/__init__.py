@@ -30,7 +30,7 @@ I8G_RELU = 1
 I8G_HASH = 2
 K_MAX = 133144
 EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_workspace_bytes",
-            "output_hash", "i8g_status_string", "i8g_version")
+            "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version")
 
 _lib = None
 _ws = {}
@@ -67,6 +67,8 @@ def load():
     lib.gemm_i8_workspace_bytes.restype = c_sz
     lib.output_hash.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
     lib.output_hash.restype = ctypes.c_int
+    lib.output_hash_workspace_bytes.argtypes = []
+    lib.output_hash_workspace_bytes.restype = c_sz
     lib.i8g_status_string.argtypes = [ctypes.c_int]
     lib.i8g_status_string.restype = ctypes.c_char_p
     lib.i8g_version.argtypes = []
@@ -138,13 +140,13 @@ def workspace_bytes(M, N, K):
 
 
 def _workspace(device, nbytes):
-    """Zero-filled workspace per (device, stream); the library leaves it
-    zeroed after every call, so it is cleared only when first allocated."""
+    """Scratch buffer per (device, stream), grown on demand; the library
+    needs no particular contents in it."""
     key = (device.index if device.index is not None else torch.cuda.current_device(),
            torch.cuda.current_stream(device).cuda_stream)
     ws = _ws.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws[key] = ws
     return ws
 
@@ -182,7 +184,7 @@ def output_hash(C):
     _req_matrix(C, torch.float32, "C")
     M, N = C.shape
     h = torch.zeros(1, dtype=torch.int64, device=C.device)
-    ws = _workspace(C.device, 256)
+    ws = _workspace(C.device, int(load().output_hash_workspace_bytes()))
     _check(load().output_hash(_ptr(C), M, N, max(C.stride(0), N, 1), _ptr(h),
                               ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(C)))
     return h

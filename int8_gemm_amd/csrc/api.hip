@@ -61,10 +61,12 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_
 }
 
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return sizeof(WsHeader);
-  GemmPlan plan = plan_gemm(M, N, K);
-  return plan.workspace_bytes;
+  if (M <= 0 || N <= 0) return 256;
+  GemmPlan plan = plan_gemm(M, N, K > 0 ? K : 1);
+  return plan.workspace_bytes > 256 ? plan.workspace_bytes : 256;
 }
+
+size_t output_hash_workspace_bytes(void) { return (size_t)kHashMaxParts * 8; }
 
 int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,
                         int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K, float* C,
@@ -78,10 +80,10 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
   if (K > I8G_K_MAX) return I8G_EKRANGE;
   if (!workspace || ((uintptr_t)workspace % 256) != 0) return I8G_EWORKSPACE;
   if (M == 0 || N == 0) {
-    if (workspace_bytes < sizeof(WsHeader)) return I8G_EWORKSPACE;
-    if (want_hash) return hip_status(launch_output_hash(C, M, N, ldc, hash,
-                                                        reinterpret_cast<WsHeader*>(workspace),
-                                                        as_stream(stream)));
+    if (workspace_bytes < 256) return I8G_EWORKSPACE;
+    if (want_hash)
+      return hip_status(launch_hash_finalize(reinterpret_cast<unsigned long long*>(workspace), 0, M,
+                                             N, hash, as_stream(stream)));
     return I8G_OK;
   }
   if (!C || !s_row || !s_col || ldc < N) return I8G_EINVAL;
@@ -113,8 +115,7 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
   p.relu = (flags & I8G_RELU) ? 1 : 0;
   p.do_hash = want_hash ? 1 : 0;
   char* ws = reinterpret_cast<char*>(workspace);
-  p.ws = reinterpret_cast<WsHeader*>(ws);
-  p.tickets = reinterpret_cast<unsigned int*>(ws + plan.tickets_offset);
+  p.hash_parts = reinterpret_cast<unsigned long long*>(ws);
   p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
   p.hash_out = hash;
   return hip_status(launch_gemm(p, plan, as_stream(stream)));
@@ -124,9 +125,11 @@ int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* has
                 size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || !hash) return I8G_EINVAL;
   if (M > 0 && N > 0 && (!C || ldc < N)) return I8G_EINVAL;
-  if (!workspace || ((uintptr_t)workspace % 256) != 0 || workspace_bytes < sizeof(WsHeader))
+  if (!workspace || ((uintptr_t)workspace % 256) != 0 ||
+      workspace_bytes < output_hash_workspace_bytes())
     return I8G_EWORKSPACE;
-  return hip_status(launch_output_hash(C, M, N, ldc, hash, reinterpret_cast<WsHeader*>(workspace),
+  return hip_status(launch_output_hash(C, M, N, ldc, hash,
+                                       reinterpret_cast<unsigned long long*>(workspace),
                                        as_stream(stream)));
 }
 

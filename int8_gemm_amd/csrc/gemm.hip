@@ -13,18 +13,21 @@
 //    sub-tiles made of 32x32 MFMA blocks.  K advances in stages of 64
 //    bytes, double-buffered in LDS: global -> registers -> LDS, one barrier
 //    per stage.  Rows are 64 bytes in LDS; the 16-byte chunk index is XORed
-//    with (row/2)%4 so that a wave's 16-byte reads of 32 rows at the same
-//    chunk spread over all banks.
+//    with (row/4)%4 so that a wave's 16-byte reads of 32 rows at the same
+//    chunk spread over all 64 banks.
 //  * Workgroup ids are remapped so that consecutive tiles of one L2 (one
 //    XCD: workgroups are dealt to the 8 XCDs round-robin) are neighbours,
 //    grouped GROUP_M tile-rows at a time to share A and B in that L2.
 //  * Split-K: when there are too few tiles to fill 256 CUs, K is split; each
-//    split writes its int32 partial tile to the workspace and takes a ticket;
-//    the last split of a tile adds the others' partials (integer, exact in
-//    any order) and runs the epilogue.
+//    split writes its int32 partial tile to the workspace and a second
+//    kernel adds the splits (integer, exact in any order) and runs the
+//    epilogue.  No kernel synchronizes with another workgroup: agent-scope
+//    release/acquire would write back and invalidate the XCD's L2.
 //  * The epilogue converts, scales (row scale, then column scale, separate
 //    roundings), applies ReLU as a select (so never -0), stores f32, and
-//    accumulates the output hash S = sum c(j)*r(i)*bits(i,j) mod 2^64.
+//    computes the tile's share of the output hash S = sum c(j)*r(i)*bits(i,j)
+//    mod 2^64, stored in a per-tile slot; a one-workgroup kernel adds the
+//    slots (mod 2^64, any order) and writes H.
 #include <cmath>
 #include <cstdlib>
 
@@ -39,7 +42,13 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int BK = 64;        // bytes of K per LDS stage
 constexpr int GROUP_M = 8;    // tile-rows per L2 group
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+// LDS rows of a stage are 64 bytes (four 16-byte chunks).  gfx950's LDS has
+// 64 banks and serves a 16-byte read for 16 lanes per cycle, so the 16 rows
+// a quarter-wave reads at one chunk position must cover all 16 distinct
+// 16-byte bank groups: rows r..r+15 sit at groups 4*(r%4) + chunk', and XOR
+// with (r/4)%4 makes chunk' distinct among the rows that share r%4.
+// (Measured: 214 B/clk per CU conflict-free, 123 with (r/2)%4, 62 without.)
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 // Zero the bytes at positions >= nvalid (1..15) of a 16-byte vector.
 __device__ __forceinline__ v4i mask_tail(v4i x, int nvalid) {
@@ -81,55 +90,200 @@ __device__ __forceinline__ void map_workgroup(int wg, int total, int tiles_m, in
   tn = in_group / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
-gemm_i8_kernel(const GemmParams p) {
-  constexpr int NT = WAVES_M * WAVES_N * 64;
+// ---------------------------------------------------------------------------
+// Main loop with direct global->LDS loads (global_load_lds_dwordx4) and a
+// ring of STAGES LDS buffers: the loads for stage kt+STAGES-1 are in flight
+// while stage kt is multiplied, without staging registers.  Each load
+// instruction fills 1 KiB of LDS (64 lanes x 16 bytes, lane l at byte 16*l),
+// i.e. 16 rows of 64 bytes; the swizzle is applied on the global side: lane
+// l of a block fetches logical chunk swz(row, l%4) of its row, so the
+// physical layout is the same XOR-swizzled one the fragment reads expect
+// (swz is an involution in the chunk index).
+// A K tail shorter than one stage goes through registers (masked).
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+  // vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]).
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | (((N >> 4) & 3) << 14));
+}
+
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
+// lds + 16*l (lds must be the same for the whole wave).
+__device__ __forceinline__ void dma_load16(const int8_t* g, int8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (the fence of __syncthreads()
+// would wait for every outstanding global load, including prefetches).
+// Callers make the LDS data visible first: s_waitcnt on the counter that
+// tracks it (vmcnt for direct-to-LDS loads, lgkmcnt for ds_write).
+__device__ __forceinline__ void barrier_nofence() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Epilogue through LDS.  Each wave parks its raw int32 accumulators 32 rows
+// at a time in a private LDS slab (MFMA layout: lane = one column, 16 rows;
+// row stride WTN+8 words, so the two half-waves' rows land on disjoint
+// banks), reads the slab back row-major with 4 consecutive columns per lane,
+// and only then applies y = RN(RN(RN(acc) * s_row) * s_col), the ReLU select
+// and the hash terms r(i)*bits(y), summed per column; each lane writes 16
+// bytes per row so the lanes cover whole row segments.  With split-K the raw
+// sums are written the same way to the split's partial plane.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM][FN], int8_t* smem,
+                                             int tm, int tn, int split) {
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int STRIDE = WTN + 8;                    // words per slab row
+  constexpr int SLAB = 32 * STRIDE;                  // words per wave
+  constexpr int LPR = WTN / 4;                       // lanes per row when reading back
+  constexpr int RPI = 64 / LPR;                      // rows per read instruction
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int M = p.M, N = p.N;
+  const int col0 = tn * BN + wn * WTN;
+  const bool raw = p.splits > 1;
+  const bool relu = p.relu != 0;
+
+  int* slab = reinterpret_cast<int*>(smem) + wave * SLAB;
+  float* s_sr = reinterpret_cast<float*>(smem) + 4 * SLAB;
+  unsigned int* s_rk = reinterpret_cast<unsigned int*>(s_sr + BM);
+  unsigned long long* s_red = reinterpret_cast<unsigned long long*>(s_rk + BM);
+  // row scales and row keys of the tile (zero beyond M: such rows add nothing)
+  for (int r = tid; r < BM; r += 256) {
+    const int gr = tm * BM + r;
+    s_sr[r] = gr < M ? p.s_row[gr] : 0.0f;
+    s_rk[r] = gr < M ? hash_row_key((unsigned int)gr) : 0u;
+  }
+  // this lane's four columns in the row-major read-back
+  const int rr0 = lane / LPR, cc = (lane % LPR) * 4;
+  const int gc0 = col0 + cc;
+  float sc[4];
+  uint64_t tcol[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sc[e] = gc0 + e < N ? p.s_col[gc0 + e] : 0.0f;
+  __syncthreads();
+
+  const int64_t ld = raw ? (int64_t)N : p.ldc;
+  const bool vec = raw ? (N % 4 == 0) : ((p.ldc % 4 == 0) && (((uintptr_t)p.C & 15) == 0));
+  int* part_base = raw ? p.partials + (int64_t)split * M * N : nullptr;
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int srow = (v >> 2) * 8 + lhalf * 4 + (v & 3);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) slab[srow * STRIDE + j * 32 + lrow] = acc[i][j][v];
+    }
+    // the slab is private to this wave and LDS operations of a wave complete
+    // in order, so it can be read back without a barrier
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+      const int srow = t * RPI + rr0;
+      const int4 a = *reinterpret_cast<const int4*>(slab + srow * STRIDE + cc);
+      const int lr = wm * WTM + i * 32 + srow;
+      const int gr = tm * BM + lr;
+      const int av[4] = {a.x, a.y, a.z, a.w};
+      if (raw) {
+        if (gr < M) {
+          int* dst = part_base + (int64_t)gr * ld + gc0;
+          if (vec && gc0 + 4 <= N) {
+            *reinterpret_cast<int4*>(dst) = a;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gc0 + e < N) dst[e] = av[e];
+          }
+        }
+      } else {
+        const float sr = s_sr[lr];
+        const uint64_t rk = s_rk[lr];
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = epilogue1(av[e], sr, sc[e]);
+          if (relu) y[e] = relu_pos0(y[e]);
+          tcol[e] += rk * (uint64_t)__float_as_uint(y[e]);
+        }
+        if (gr < M) {
+          float* dst = p.C + (int64_t)gr * ld + gc0;
+          if (vec && gc0 + 4 <= N) {
+            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gc0 + e < N) dst[e] = y[e];
+          }
+        }
+      }
+    }
+  }
+  if (!raw && p.do_hash) {
+    uint64_t hsum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (gc0 + e < N) hsum += hash_col_key((uint64_t)(gc0 + e)) * tcol[e];
+    const uint64_t part = block_sum_u64<256>(hsum, s_red);
+    if (tid == 0) p.hash_parts[tm * p.tiles_n + tn] = part;
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+__global__ void __launch_bounds__(256)
+gemm_i8_dma_kernel(const GemmParams p) {
+  static_assert(WAVES_M * WAVES_N == 4, "four waves");
+  static_assert(STAGES >= 3, "the ring needs at least three stages");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int CPR = BK / 16;                       // 16-byte chunks per row
-  constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;
-  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "stage not divisible");
-  constexpr int STAGE = (BM + BN) * BK;
-  constexpr int EPI_BYTES = (2 * BM + BN) * 4 + 4 * 16;
-  constexpr int SMEM = (2 * STAGE > EPI_BYTES) ? 2 * STAGE : EPI_BYTES;
-  __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
-  __shared__ int s_flag;
+  constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  constexpr int A_INS = BM / 64, B_INS = BN / 64;     // 16-row blocks per wave per stage
+  constexpr int LPS = A_INS + B_INS;                   // load instructions per wave per stage
+  constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4 + 2 * BM * 4 + 64;
+  constexpr int SMEM = STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
   int tm, tn, split;
   map_workgroup(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.splits, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
-
   const int k_begin = split * p.k_per_split;
   int k_end = k_begin + p.k_per_split;
   if (k_end > K) k_end = K;
-  const int nk = (k_end - k_begin + BK - 1) / BK;
+  const int klen = k_end > k_begin ? k_end - k_begin : 0;
+  const int nfull = klen / BK;
+  const bool tail = (klen % BK) != 0;
 
-  // Per-thread global load sources (rows clamped into range: rows past M or
-  // N are computed on duplicated data and never stored).
-  const int8_t* a_src[A_LD];
-  const int8_t* b_src[B_LD];
-  int a_off[A_LD], b_off[B_LD], a_ck[A_LD], b_ck[B_LD];
+  // global sources of this lane's 16-byte chunks (rows clamped into range)
+  const int r_in = lane >> 2, slot = lane & 3;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave id in a scalar register
+  const int8_t* ga[A_INS];
+  const int8_t* gb[B_INS];
 #pragma unroll
-  for (int q = 0; q < A_LD; ++q) {
-    int c = tid + q * NT, row = c / CPR, ck = c % CPR;
+  for (int q = 0; q < A_INS; ++q) {
+    const int row = (q * 4 + wave) * 16 + r_in;
     int gr = m0 + row; gr = gr < M ? gr : M - 1;
-    a_src[q] = p.A + (int64_t)gr * p.lda;
-    a_ck[q] = ck * 16;
-    a_off[q] = row * BK + (swz(row, ck) << 4);
+    ga[q] = p.A + (int64_t)gr * p.lda + k_begin + (swz(row, slot) << 4);
   }
 #pragma unroll
-  for (int q = 0; q < B_LD; ++q) {
-    int c = tid + q * NT, row = c / CPR, ck = c % CPR;
+  for (int q = 0; q < B_INS; ++q) {
+    const int row = (q * 4 + wave) * 16 + r_in;
     int gr = n0 + row; gr = gr < N ? gr : N - 1;
-    b_src[q] = p.B + (int64_t)gr * p.ldb;
-    b_ck[q] = ck * 16;
-    b_off[q] = BM * BK + row * BK + (swz(row, ck) << 4);
+    gb[q] = p.B + (int64_t)gr * p.ldb + k_begin + (swz(row, slot) << 4);
   }
+  auto issue = [&](int buf, int kt) {
+    int8_t* base = smem + buf * STAGE + wave_s * 1024;
+#pragma unroll
+    for (int q = 0; q < A_INS; ++q) dma_load16(ga[q] + kt * BK, base + q * 4096);
+#pragma unroll
+    for (int q = 0; q < B_INS; ++q) dma_load16(gb[q] + kt * BK, base + A_BYTES + q * 4096);
+  };
 
   v16i acc[FM][FN];
 #pragma unroll
@@ -139,172 +293,220 @@ gemm_i8_kernel(const GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  v4i ra[A_LD], rb[B_LD];
-  if (nk > 0) {
-#pragma unroll
-    for (int q = 0; q < A_LD; ++q) ra[q] = load_chunk(a_src[q], k_begin + a_ck[q], k_end);
-#pragma unroll
-    for (int q = 0; q < B_LD; ++q) rb[q] = load_chunk(b_src[q], k_begin + b_ck[q], k_end);
-#pragma unroll
-    for (int q = 0; q < A_LD; ++q) *reinterpret_cast<v4i*>(smem + a_off[q]) = ra[q];
-#pragma unroll
-    for (int q = 0; q < B_LD; ++q) *reinterpret_cast<v4i*>(smem + b_off[q]) = rb[q];
-  }
-  __syncthreads();
-
-  // LDS read offsets of this lane's MFMA operands (stage-relative).
   const int lrow = lane & 31, lhalf = lane >> 5;
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = (kt & 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int kn = k_begin + (kt + 1) * BK;
+  // per-lane LDS offsets (stage-relative) of the fragments of k-steps 0 and 1
+  int offa[2][FM], offb[2][FN];
 #pragma unroll
-      for (int q = 0; q < A_LD; ++q) ra[q] = load_chunk(a_src[q], kn + a_ck[q], k_end);
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int q = 0; q < B_LD; ++q) rb[q] = load_chunk(b_src[q], kn + b_ck[q], k_end);
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * WTM + i * 32 + lrow;
+      offa[s][i] = row * BK + (swz(row, s * 2 + lhalf) << 4);
     }
 #pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      const int ck = s * 2 + lhalf;
-      v4i af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        int row = wm * WTM + i * 32 + lrow;
-        af[i] = *reinterpret_cast<const v4i*>(smem + cur + row * BK + (swz(row, ck) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int row = wn * WTN + j * 32 + lrow;
-        bf[j] = *reinterpret_cast<const v4i*>(smem + cur + BM * BK + row * BK + (swz(row, ck) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WTN + j * 32 + lrow;
+      offb[s][j] = A_BYTES + row * BK + (swz(row, s * 2 + lhalf) << 4);
     }
-    if (more) {
-      const int nxt = STAGE - cur;
-#pragma unroll
-      for (int q = 0; q < A_LD; ++q) *reinterpret_cast<v4i*>(smem + nxt + a_off[q]) = ra[q];
-#pragma unroll
-      for (int q = 0; q < B_LD; ++q) *reinterpret_cast<v4i*>(smem + nxt + b_off[q]) = rb[q];
-    }
-    __syncthreads();
   }
-
-  // ---- split-K: exchange int32 partial tiles through the workspace ----
-  const int tile = tm * p.tiles_n + tn;
-  if (p.splits > 1) {
-    v4i* mine = reinterpret_cast<v4i*>(p.partials) +
-                ((int64_t)tile * p.splits + split) * (BM * BN / 4);
+  auto load_frags = [&](int buf, int s, v4i (&fa)[FM], v4i (&fb)[FN]) {
+    const int8_t* sb = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const v4i*>(sb + offa[s][i]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const v4i*>(sb + offb[s][j]);
+  };
+  auto mfmas = [&](const v4i (&fa)[FM], const v4i (&fb)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // Ask the scheduler to alternate the FM+FN fragment reads of the next
+  // k-step with this k-step's MFMAs (1 MFMA, 1 read, ...), so the reads stay
+  // queued behind MFMA work.  Measured against issuing all reads first: the
+  // alternation is 7-10% faster.
+  auto interleave = [&]() {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          mine[((i * FN + j) * 4 + q) * NT + tid] = v;
-        }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      unsigned int t = __hip_atomic_fetch_add(p.tickets + tile, 1u, __ATOMIC_ACQ_REL,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = (t == (unsigned int)(p.splits - 1));
-      if (s_flag) __hip_atomic_store(p.tickets + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < FM + FN; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-    for (int o = 0; o < p.splits; ++o) {
-      if (o == split) continue;
-      const v4i* other = reinterpret_cast<const v4i*>(p.partials) +
-                         ((int64_t)tile * p.splits + o) * (BM * BN / 4);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v4i v = __builtin_nontemporal_load(other + ((i * FN + j) * 4 + q) * NT + tid);
-            acc[i][j][4 * q] += v[0];
-            acc[i][j][4 * q + 1] += v[1];
-            acc[i][j][4 * q + 2] += v[2];
-            acc[i][j][4 * q + 3] += v[3];
-          }
-    }
-  }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+  };
 
-  // ---- epilogue: scales, keys and the hash ----
-  float* s_sr = reinterpret_cast<float*>(smem);
-  unsigned int* s_rk = reinterpret_cast<unsigned int*>(smem + BM * 4);
-  float* s_sc = reinterpret_cast<float*>(smem + 2 * BM * 4);
-  unsigned long long* s_red = reinterpret_cast<unsigned long long*>(smem + (2 * BM + BN) * 4);
-  for (int r = tid; r < BM; r += NT) {
-    int gr = m0 + r;
-    s_sr[r] = gr < M ? p.s_row[gr] : 0.0f;
-    s_rk[r] = hash_row_key((unsigned int)gr);
+  v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  if (nfull > 0) {
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < nfull) issue(st, st);
+    if (nfull >= STAGES - 1) wait_vmcnt<(STAGES - 2) * LPS>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    load_frags(0, 0, fa0, fb0);
+    int kt = 0;
+    // steady state: every iteration issues a stage and prepares the next one
+    for (; kt + STAGES - 1 < nfull; ++kt) {
+      const int buf = kt % STAGES;
+      load_frags(buf, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(STAGES - 3) * LPS>();                   // stage kt+1 landed (this wave)
+      barrier_nofence();                                  // ... and for every wave
+      issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1); // into the buffer read at kt-1
+      load_frags((kt + 1) % STAGES, 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // drain: the remaining stages are already in flight
+    for (; kt < nfull; ++kt) {
+      const int buf = kt % STAGES;
+      load_frags(buf, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      if (kt + 1 < nfull) {
+        wait_vmcnt<0>();
+        barrier_nofence();
+        load_frags((kt + 1) % STAGES, 0, fa0, fb0);
+      }
+      mfmas(fa1, fb1);
+    }
   }
-  for (int c = tid; c < BN; c += NT) {
-    int gc = n0 + c;
-    s_sc[c] = gc < N ? p.s_col[gc] : 0.0f;
+  if (tail) {
+    // last partial stage: masked register loads into a free buffer
+    __syncthreads();
+    const int buf = nfull % STAGES;
+    int8_t* base = smem + buf * STAGE;
+    const int k0 = k_begin + nfull * BK;
+    constexpr int CPR = BK / 16;
+#pragma unroll
+    for (int q = 0; q < (BM + BN) * CPR / 256; ++q) {
+      const int c = tid + q * 256, row = c / CPR, ck = c % CPR;
+      const bool is_a = row < BM;
+      const int r = is_a ? row : row - BM;
+      int gr = (is_a ? m0 : n0) + r;
+      const int lim = is_a ? M : N;
+      gr = gr < lim ? gr : lim - 1;
+      const int8_t* src = is_a ? p.A + (int64_t)gr * p.lda : p.B + (int64_t)gr * p.ldb;
+      const v4i v = load_chunk(src, k0 + ck * 16, k_end);
+      *reinterpret_cast<v4i*>(base + (is_a ? 0 : A_BYTES) + r * BK + (swz(r, ck) << 4)) = v;
+    }
+    __syncthreads();
+    load_frags(buf, 0, fa0, fb0);
+    load_frags(buf, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    mfmas(fa1, fb1);
   }
+  wait_vmcnt<0>();
   __syncthreads();
+  epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, tm, tn, split);
+}
 
+// ---------------------------------------------------------------------------
+// split-K combine: acc = sum over splits (exact), then the same epilogue and
+// hash shares as the GEMM kernel; each thread owns 4 consecutive columns of a
+// band of COMB_ROWS rows.
+// ---------------------------------------------------------------------------
+constexpr int COMB_ROWS = 32;
+
+__global__ void __launch_bounds__(256)
+splitk_combine_kernel(const GemmParams p) {
+  __shared__ unsigned long long red[4];
+  const int M = p.M, N = p.N;
+  const int tid = threadIdx.x;
+  const int c0 = (blockIdx.x * 256 + tid) * 4;
+  const int r0 = blockIdx.y * COMB_ROWS;
+  const int r1 = r0 + COMB_ROWS < M ? r0 + COMB_ROWS : M;
   const bool relu = p.relu != 0;
-  const bool do_hash = p.do_hash != 0;
-  uint64_t hsum = 0;
+  const int64_t plane = (int64_t)M * N;
+  uint64_t t[4] = {0, 0, 0, 0};
+  float sc[4];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int lc = wn * WTN + j * 32 + lrow;
-    const int gc = n0 + lc;
-    const bool col_ok = gc < N;
-    const float sc = s_sc[lc];
-    uint64_t tcol = 0;
+  for (int e = 0; e < 4; ++e) sc[e] = (c0 + e < N) ? p.s_col[c0 + e] : 0.0f;
+  const bool vec = (N % 4 == 0) && (p.ldc % 4 == 0) && (((uintptr_t)p.C & 15) == 0);
+  if (c0 < N) {
+    for (int r = r0; r < r1; ++r) {
+      int a[4] = {0, 0, 0, 0};
+      const int* src = p.partials + (int64_t)r * N + c0;
+      for (int sp = 0; sp < p.splits; ++sp) {
+        if (vec) {
+          const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + sp * plane));
+          a[0] += v[0]; a[1] += v[1]; a[2] += v[2]; a[3] += v[3];
+        } else {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = wm * WTM + i * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
-        const int gr = m0 + lr;
-        if (col_ok && gr < M) {
-          float y = epilogue1(acc[i][j][v], s_sr[lr], sc);
-          if (relu) y = relu_pos0(y);
-          p.C[(int64_t)gr * p.ldc + gc] = y;
-          tcol += (uint64_t)s_rk[lr] * (uint64_t)__float_as_uint(y);
+          for (int e = 0; e < 4; ++e)
+            if (c0 + e < N) a[e] += src[sp * plane + e];
         }
       }
+      const float sr = p.s_row[r];
+      const uint64_t rk = hash_row_key((uint32_t)r);
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = epilogue1(a[e], sr, sc[e]);
+        if (relu) y[e] = relu_pos0(y[e]);
+        t[e] += rk * (uint64_t)__float_as_uint(y[e]);
+      }
+      float* dst = p.C + (int64_t)r * p.ldc + c0;
+      if (vec) {
+        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < N) dst[e] = y[e];
+      }
     }
-    if (do_hash && col_ok) hsum += hash_col_key((uint64_t)gc) * tcol;
   }
-  if (do_hash) {
-    hsum = wave_sum_u64(hsum);
-    if (lane == 0) s_red[wave] = hsum;
-    __syncthreads();
-    if (tid == 0) {
-      uint64_t part = 0;
-      for (int w = 0; w < NT / 64; ++w) part += s_red[w];
-      hash_commit(p.ws, part, (unsigned int)(p.tiles_m * p.tiles_n), (uint64_t)M, (uint64_t)N,
-                  p.hash_out, nullptr);
-    }
-  }
+  uint64_t part = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (c0 + e < N) part += hash_col_key((uint64_t)(c0 + e)) * t[e];
+  part = block_sum_u64<256>(part, red);
+  if (p.do_hash && tid == 0) p.hash_parts[blockIdx.y * gridDim.x + blockIdx.x] = part;
+}
+
+// H = fmix64(sum of the shares ^ fmix64(M*2^32 + N)), one workgroup.
+__global__ void __launch_bounds__(256)
+hash_finalize_kernel(const unsigned long long* parts, int n, uint64_t M, uint64_t N,
+                     uint64_t* hash_out) {
+  __shared__ unsigned long long red[4];
+  uint64_t s = 0;
+  for (int i = threadIdx.x; i < n; i += 256) s += parts[i];
+  s = block_sum_u64<256>(s, red);
+  if (threadIdx.x == 0) *hash_out = hash_finalize(s, M, N);
+}
+
+hipError_t launch_hash_finalize(const unsigned long long* parts, int n, int64_t M, int64_t N,
+                                uint64_t* hash_out, hipStream_t stream) {
+  hipLaunchKernelGGL(hash_finalize_kernel, dim3(1), dim3(256), 0, stream, parts, n, (uint64_t)M,
+                     (uint64_t)N, hash_out);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // host side: plan and launch
 // ---------------------------------------------------------------------------
+// Tile configurations: macro tile, LDS stages, workgroups resident per CU,
+// and the int8 MAC rate one workgroup sustains in the steady-state loop
+// (measured on MI355X with operands streaming through L2: LM-head weight
+// gradient 768x50304x8192, down-projection 8192x768x3072).
 struct TileCfg {
-  int bm, bn, nt;
+  int bm, bn, stages, per_cu;
+  double wg_macs;   // MAC/s of one resident workgroup
 };
-static const TileCfg kCfgs[] = {{256, 256, 256}, {256, 128, 256}, {128, 128, 256}};
+static const TileCfg kCfgs[] = {
+    {256, 256, 4, 1, 4.0e12},
+    {256, 128, 4, 1, 3.0e12},
+    {128, 128, 4, 2, 1.45e12},
+    {256, 256, 5, 1, 3.9e12},
+};
+constexpr int kNumCfgs = 4;
 
 // Optional overrides for tests (the output never depends on the plan):
-// I8G_FORCE_TILE = 0 (256x256), 1 (256x128) or 2 (128x128); I8G_FORCE_SPLITS
-// = number of K splits (clamped so that no split is empty).
+// I8G_FORCE_TILE = index into kCfgs; I8G_FORCE_SPLITS = number of K splits
+// (clamped so that no split is empty).
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   return (v && *v) ? atoi(v) : dflt;
@@ -315,31 +517,34 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0) return best;
   const int force_tile = env_int("I8G_FORCE_TILE", -1);
   const int force_splits = env_int("I8G_FORCE_SPLITS", 0);
-  const double cus = 256.0;
+  // Estimated seconds: rounds of resident workgroups x (MAC time of one
+  // workgroup's share + the time to write its output tile at ~20 GB/s per
+  // CU; with two workgroups per CU one's stores overlap the other's MFMAs),
+  // plus the split-K partial round trip.
+  const double cu_out_bw = 20e9;
+  const double mem_bw = 4.0e12;
   double best_cost = 1e300;
-  for (int c = 0; c < 3; ++c) {
-    if (force_tile >= 0 ? c != force_tile : c == 0) continue;   // 256x256 only on request
+  for (int c = 0; c < kNumCfgs; ++c) {
+    if (force_tile >= 0 && c != force_tile) continue;
+    if (force_tile < 0 && c == 3) continue;        // the 5-stage ring only on request
     const TileCfg& t = kCfgs[c];
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = tm * tn;
-    // slots: workgroups resident per CU (256x256 uses more registers)
-    const double slots = cus * (t.bm * t.bn >= 65536 ? 1.0 : 2.0);
-    // relative MAC rate of one workgroup of this tile shape
-    const double eff = (t.bm * t.bn >= 65536) ? 1.0 : (t.bm * t.bn >= 32768 ? 0.5 : 0.25);
+    const double slots = 256.0 * t.per_cu;
     const int64_t kstages = (K + BK - 1) / BK;
     for (int s = 1; s <= 16; ++s) {
       if (force_splits > 0) {
         if (s != (force_splits < kstages ? force_splits : (int)kstages)) continue;
-      } else {
-        if (s > 1 && kstages / s < 8) break;         // keep >= 8 stages per split
-        if (s > 1 && tiles * s > 4 * (int64_t)slots) break;
+      } else if (s > 1 && kstages / s < 16) {
+        break;                                      // keep >= 16 stages per split
       }
       const int64_t kps_st = (kstages + s - 1) / s;
       const int s_eff = (int)((kstages + kps_st - 1) / kps_st);   // no empty split
-      const double waves = std::ceil((double)(tiles * s_eff) / slots);
-      double cost = waves * (double)kps_st / eff;
-      cost += (s_eff > 1 ? 0.05 * cost : 0.0);       // partial exchange
-      cost += (double)tiles * t.bm * t.bn * 1e-9;    // prefer less padding
+      const double rounds = std::ceil((double)(tiles * s_eff) / slots);
+      const double tile_s = (double)t.bm * t.bn * kps_st * BK / t.wg_macs +
+                            (double)t.bm * t.bn * 4 / cu_out_bw;
+      double cost = rounds * tile_s;
+      if (s_eff > 1) cost += (double)s_eff * M * N * 8 / mem_bw + 5e-6;
       if (cost < best_cost * 0.999) {
         best_cost = cost;
         best.cfg = c;
@@ -352,17 +557,22 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
       }
     }
   }
-  if (best.bm == 0) {   // unreachable: the 128x128, one-split plan is always a candidate
+  if (best.bm == 0) {   // unreachable: every configuration has a one-split plan
     best.cfg = 2; best.bm = best.bn = 128;
     best.tiles_m = (int)((M + 127) / 128); best.tiles_n = (int)((N + 127) / 128);
     best.splits = 1; best.k_per_split = (int)((K + BK - 1) / BK * BK);
   }
-  int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
-  size_t bytes = sizeof(WsHeader);
-  bytes += ((size_t)tiles * 4 + 255) / 256 * 256;            // tickets
-  best.tickets_offset = sizeof(WsHeader);
+  const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
+  if (best.splits > 1) {
+    best.comb_x = (int)((N + 1023) / 1024);
+    best.comb_y = (int)((M + COMB_ROWS - 1) / COMB_ROWS);
+    best.hash_parts = best.comb_x * best.comb_y;
+  } else {
+    best.hash_parts = (int)tiles;
+  }
+  size_t bytes = ((size_t)best.hash_parts * 8 + 255) / 256 * 256;
   best.partials_offset = bytes;
-  if (best.splits > 1) bytes += (size_t)tiles * best.splits * best.bm * best.bn * 4;
+  if (best.splits > 1) bytes += (size_t)best.splits * M * N * 4;
   best.workspace_bytes = bytes;
   return best;
 }
@@ -371,15 +581,22 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
   const unsigned int grid = (unsigned int)((int64_t)plan.tiles_m * plan.tiles_n * plan.splits);
   switch (plan.cfg) {
     case 0:
-      hipLaunchKernelGGL((gemm_i8_kernel<256, 256, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
       break;
     case 1:
-      hipLaunchKernelGGL((gemm_i8_kernel<256, 128, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
       break;
     default:
-      hipLaunchKernelGGL((gemm_i8_kernel<128, 128, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 5>), dim3(grid), dim3(256), 0, stream, p);
       break;
   }
+  if (plan.splits > 1)
+    hipLaunchKernelGGL(splitk_combine_kernel, dim3(plan.comb_x, plan.comb_y), dim3(256), 0, stream, p);
+  if (p.do_hash)
+    return launch_hash_finalize(p.hash_parts, plan.hash_parts, p.M, p.N, p.hash_out, stream);
   return hipGetLastError();
 }
 

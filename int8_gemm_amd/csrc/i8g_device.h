@@ -112,35 +112,18 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 
-// Workspace header shared by the GEMM and the hash kernels.  It must start
-// zeroed; the last workgroup of a call returns it to zero.
-struct WsHeader {
-  unsigned long long hash_sum;   // S, accumulated with device-scope atomics
-  unsigned int done;             // workgroups that have added their part of S
-  unsigned int pad[61];          // keeps the header 256 bytes
-};
-static_assert(sizeof(WsHeader) == 256, "workspace header must be 256 bytes");
-
-// Adds this workgroup's part of S, and lets the last workgroup of the grid
-// write H and reset the header.  Call from every thread of the workgroup
-// after `part` holds the workgroup total in thread 0 (other threads pass 0).
-// `red` is LDS scratch of at least one uint32.
-__device__ __forceinline__ void hash_commit(WsHeader* ws, uint64_t part, unsigned int n_groups,
-                                            uint64_t M, uint64_t N, uint64_t* hash_out,
-                                            unsigned int* red) {
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(&ws->hash_sum, (unsigned long long)part, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    unsigned int t = __hip_atomic_fetch_add(&ws->done, 1u, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    if (t == n_groups - 1) {
-      unsigned long long s = __hip_atomic_exchange(&ws->hash_sum, 0ull, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ws->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *hash_out = hash_finalize(s, M, N);
-    }
-  }
-  (void)red;
+// Sum of a 64-bit value over a workgroup of NT threads (mod 2^64); the
+// result is valid in thread 0.  `red` is LDS scratch of NT/64 words.
+template <int NT>
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, unsigned long long* red) {
+  v = wave_sum_u64(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint64_t t = 0;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < NT / 64; ++w) t += red[w];
+  return t;
 }
 
 }  // namespace i8g

@@ -7,8 +7,6 @@
 
 namespace i8g {
 
-struct WsHeader;
-
 struct GemmParams {
   const int8_t* A;          // QA, M x K, K contiguous
   const int8_t* B;          // QBt, N x K, K contiguous
@@ -19,9 +17,8 @@ struct GemmParams {
   int M, N, K;
   int tiles_m, tiles_n, splits, k_per_split;
   int relu, do_hash;
-  WsHeader* ws;
-  unsigned int* tickets;
-  int* partials;
+  unsigned long long* hash_parts;   // per-tile (or per-combine-group) shares of S
+  int* partials;                    // split-K int32 partial sums, [split][M][N]
   uint64_t* hash_out;
 };
 
@@ -31,8 +28,9 @@ struct GemmPlan {
   int tiles_m, tiles_n;
   int splits;
   int k_per_split;          // bytes of K per split (multiple of 64)
-  size_t tickets_offset;
-  size_t partials_offset;
+  int comb_x, comb_y;       // split-K combine grid
+  int hash_parts;           // number of shares of S written before the finalize
+  size_t partials_offset;   // hash shares at offset 0, split partials here
   size_t workspace_bytes;
 };
 
@@ -44,6 +42,11 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                 int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream);
 hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
-                              uint64_t* hash, WsHeader* ws, hipStream_t stream);
+                              uint64_t* hash, unsigned long long* parts, hipStream_t stream);
+hipError_t launch_hash_finalize(const unsigned long long* parts, int n, int64_t M, int64_t N,
+                                uint64_t* hash_out, hipStream_t stream);
+
+// output_hash uses at most this many shares (its workspace is 8 bytes each)
+constexpr int kHashMaxParts = 2048;
 
 }  // namespace i8g

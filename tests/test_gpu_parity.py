@@ -164,7 +164,7 @@ def test_w4_adversarial_sweep(g, chunk):
             assert np.all(got["C"].view(U32) >> 31 == 0)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("tile", list(range(4)))
 def test_tile_and_split_invariance(g, tile):
     """Different tile shapes and K splits give byte-identical outputs (integer
     accumulation is associative), all equal to the oracle."""
@@ -262,23 +262,24 @@ def test_error_statuses(g):
     assert rc == 1
 
 
-def test_workspace_control_words_reset(g):
-    """The workspace header returns to zero after each call, and the same
-    workspace serves repeated split-K calls (tickets reset), with identical
-    bytes each time."""
-    say("workspace control words")
+def test_workspace_contents_do_not_matter(g):
+    """The workspace is scratch: filling it with garbage before each call
+    changes no byte; repeated split-K calls give identical bytes."""
+    say("workspace garbage")
     rng = np.random.default_rng(79)
     A = rng.standard_normal((700, 9000)).astype(F32)
     B = rng.standard_normal((9000, 300)).astype(F32)
-    first = run_method(g, A, B, relu=False)
-    for ws in g._ws.values():
-        assert int(torch.count_nonzero(ws[:256]).item()) == 0
-    for _ in range(3):
-        again = run_method(g, A, B, relu=False)
-        assert_bits(again["C"], first["C"], "repeat")
-        assert again["hash"] == first["hash"]
     C, *_ = ref.blockscaled_gemm(A, B, False)
-    assert_bits(first["C"], C, "C")
+    for it in range(3):
+        for ws in g._ws.values():
+            ws.random_(0, 256)
+        os.environ["I8G_FORCE_SPLITS"] = "3"
+        try:
+            got = run_method(g, A, B, relu=False)
+        finally:
+            os.environ.pop("I8G_FORCE_SPLITS", None)
+        assert_bits(got["C"], C, f"C call {it}")
+        assert got["hash"] == hashref.output_hash(C)
 
 
 def test_metamorphic_on_gpu(g):
