@@ -114,6 +114,7 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
   p.k_per_split = plan.k_per_split;
   p.relu = (flags & I8G_RELU) ? 1 : 0;
   p.do_hash = want_hash ? 1 : 0;
+  p.stream_out = ((double)M * (double)N * 4.0 > 128.0 * 1024 * 1024) ? 1 : 0;
   char* ws = reinterpret_cast<char*>(workspace);
   p.hash_parts = reinterpret_cast<unsigned long long*>(ws);
   p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);

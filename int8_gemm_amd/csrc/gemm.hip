@@ -125,6 +125,18 @@ __device__ __forceinline__ void barrier_nofence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Output rows are written once by this kernel.  A large output (more than
+// half of the 256 MB last-level cache) is streamed past the caches
+// (nontemporal); a smaller one is stored normally so that a following
+// kernel (e.g. the next layer's quantize pass) can still find it in cache.
+__device__ __forceinline__ void store_out4(float* dst, float a, float b, float c, float d,
+                                           bool stream) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f v = {a, b, c, d};
+  if (stream) __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(dst));
+  else *reinterpret_cast<v4f*>(dst) = v;
+}
+
 // Epilogue through LDS.  Each wave parks its raw int32 accumulators 32 rows
 // at a time in a private LDS slab (MFMA layout: lane = one column, 16 rows;
 // row stride WTN+8 words, so the two half-waves' rows land on disjoint
@@ -141,6 +153,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   constexpr int SLAB = 32 * STRIDE;                  // words per wave
   constexpr int LPR = WTN / 4;                       // lanes per row when reading back
   constexpr int RPI = 64 / LPR;                      // rows per read instruction
+  constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -148,13 +161,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   const int col0 = tn * BN + wn * WTN;
   const bool raw = p.splits > 1;
   const bool relu = p.relu != 0;
+  const bool stream = p.stream_out != 0;
 
   int* slab = reinterpret_cast<int*>(smem) + wave * SLAB;
-  float* s_sr = reinterpret_cast<float*>(smem) + 4 * SLAB;
+  float* s_sr = reinterpret_cast<float*>(smem) + NWAVES * SLAB;
   unsigned int* s_rk = reinterpret_cast<unsigned int*>(s_sr + BM);
   unsigned long long* s_red = reinterpret_cast<unsigned long long*>(s_rk + BM);
   // row scales and row keys of the tile (zero beyond M: such rows add nothing)
-  for (int r = tid; r < BM; r += 256) {
+  for (int r = tid; r < BM; r += NT) {
     const int gr = tm * BM + r;
     s_sr[r] = gr < M ? p.s_row[gr] : 0.0f;
     s_rk[r] = gr < M ? hash_row_key((unsigned int)gr) : 0u;
@@ -213,7 +227,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
         if (gr < M) {
           float* dst = p.C + (int64_t)gr * ld + gc0;
           if (vec && gc0 + 4 <= N) {
-            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+            store_out4(dst, y[0], y[1], y[2], y[3], stream);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -228,22 +242,24 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (gc0 + e < N) hsum += hash_col_key((uint64_t)(gc0 + e)) * tcol[e];
-    const uint64_t part = block_sum_u64<256>(hsum, s_red);
+    const uint64_t part = block_sum_u64<NT>(hsum, s_red);
     if (tid == 0) p.hash_parts[tm * p.tiles_n + tn] = part;
   }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_i8_dma_kernel(const GemmParams p) {
-  static_assert(WAVES_M * WAVES_N == 4, "four waves");
+  constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
+  static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves");
   static_assert(STAGES >= 3, "the ring needs at least three stages");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
-  constexpr int A_INS = BM / 64, B_INS = BN / 64;     // 16-row blocks per wave per stage
+  constexpr int A_INS = BM / (16 * NWAVES), B_INS = BN / (16 * NWAVES);   // 16-row blocks per wave
+  static_assert(A_INS * 16 * NWAVES == BM && B_INS * 16 * NWAVES == BN, "rows per stage");
   constexpr int LPS = A_INS + B_INS;                   // load instructions per wave per stage
-  constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4 + 2 * BM * 4 + 64;
+  constexpr int EPI_BYTES = NWAVES * 32 * (WTN + 8) * 4 + 2 * BM * 4 + 128;
   constexpr int SMEM = STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
@@ -267,22 +283,22 @@ gemm_i8_dma_kernel(const GemmParams p) {
   const int8_t* gb[B_INS];
 #pragma unroll
   for (int q = 0; q < A_INS; ++q) {
-    const int row = (q * 4 + wave) * 16 + r_in;
+    const int row = (q * NWAVES + wave) * 16 + r_in;
     int gr = m0 + row; gr = gr < M ? gr : M - 1;
     ga[q] = p.A + (int64_t)gr * p.lda + k_begin + (swz(row, slot) << 4);
   }
 #pragma unroll
   for (int q = 0; q < B_INS; ++q) {
-    const int row = (q * 4 + wave) * 16 + r_in;
+    const int row = (q * NWAVES + wave) * 16 + r_in;
     int gr = n0 + row; gr = gr < N ? gr : N - 1;
     gb[q] = p.B + (int64_t)gr * p.ldb + k_begin + (swz(row, slot) << 4);
   }
   auto issue = [&](int buf, int kt) {
     int8_t* base = smem + buf * STAGE + wave_s * 1024;
 #pragma unroll
-    for (int q = 0; q < A_INS; ++q) dma_load16(ga[q] + kt * BK, base + q * 4096);
+    for (int q = 0; q < A_INS; ++q) dma_load16(ga[q] + kt * BK, base + q * NWAVES * 1024);
 #pragma unroll
-    for (int q = 0; q < B_INS; ++q) dma_load16(gb[q] + kt * BK, base + A_BYTES + q * 4096);
+    for (int q = 0; q < B_INS; ++q) dma_load16(gb[q] + kt * BK, base + A_BYTES + q * NWAVES * 1024);
   };
 
   v16i acc[FM][FN];
@@ -382,8 +398,8 @@ gemm_i8_dma_kernel(const GemmParams p) {
     const int k0 = k_begin + nfull * BK;
     constexpr int CPR = BK / 16;
 #pragma unroll
-    for (int q = 0; q < (BM + BN) * CPR / 256; ++q) {
-      const int c = tid + q * 256, row = c / CPR, ck = c % CPR;
+    for (int q = 0; q < (BM + BN) * CPR / NT; ++q) {
+      const int c = tid + q * NT, row = c / CPR, ck = c % CPR;
       const bool is_a = row < BM;
       const int r = is_a ? row : row - BM;
       int gr = (is_a ? m0 : n0) + r;
@@ -497,10 +513,10 @@ struct TileCfg {
   double wg_macs;   // MAC/s of one resident workgroup
 };
 static const TileCfg kCfgs[] = {
-    {256, 256, 4, 1, 4.0e12},
-    {256, 128, 4, 1, 3.0e12},
-    {128, 128, 4, 2, 1.45e12},
-    {256, 256, 5, 1, 3.9e12},
+    {256, 256, 4, 1, 4.5e12},   // eight waves (two per SIMD), 128x64 each
+    {256, 128, 4, 1, 3.0e12},   // four waves, 128x64 each
+    {128, 128, 4, 2, 1.25e12},  // four waves, 64x64 each
+    {256, 256, 4, 1, 4.0e12},   // four waves, 128x128 each (not chosen by default)
 };
 constexpr int kNumCfgs = 4;
 
@@ -526,7 +542,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   double best_cost = 1e300;
   for (int c = 0; c < kNumCfgs; ++c) {
     if (force_tile >= 0 && c != force_tile) continue;
-    if (force_tile < 0 && c == 3) continue;        // the 5-stage ring only on request
+    if (force_tile < 0 && c == 3) continue;        // dominated by config 0; tests only
     const TileCfg& t = kCfgs[c];
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = tm * tn;
@@ -581,7 +597,7 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
   const unsigned int grid = (unsigned int)((int64_t)plan.tiles_m * plan.tiles_n * plan.splits);
   switch (plan.cfg) {
     case 0:
-      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 4, 4>), dim3(grid), dim3(512), 0, stream, p);
       break;
     case 1:
       hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
@@ -590,7 +606,7 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
       hipLaunchKernelGGL((gemm_i8_dma_kernel<128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
       break;
     default:
-      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 5>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
       break;
   }
   if (plan.splits > 1)

@@ -17,6 +17,7 @@ struct GemmParams {
   int M, N, K;
   int tiles_m, tiles_n, splits, k_per_split;
   int relu, do_hash;
+  int stream_out;                   // store C with nontemporal hints (large outputs)
   unsigned long long* hash_parts;   // per-tile (or per-combine-group) shares of S
   int* partials;                    // split-K int32 partial sums, [split][M][N]
   uint64_t* hash_out;

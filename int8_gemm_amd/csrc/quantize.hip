@@ -12,8 +12,10 @@
 //    1024-thread workgroup per row beyond that (registers up to 65536
 //    elements, a second read from cache above).  The row max is a wave
 //    butterfly reduction (plus LDS across waves).
-//  * cols: the column max needs every row first, so it is a grid-wide
-//    reduction: zero the scale array, a column-max kernel combines
+//  * cols, up to 8192 rows: one kernel, a workgroup per column band holding
+//    the band in registers (see qcols_reg_kernel).
+//  * cols, taller: the column max needs every row first, so it is a
+//    grid-wide reduction: zero the scale array, a column-max kernel combines
 //    workgroup maxima with atomicMax on the bit patterns of |x| (for
 //    non-negative floats the integer order is the float order, so the
 //    result is exact and order-free), then a quantize kernel transposes
@@ -276,10 +278,135 @@ __global__ void qcols_scale_kernel(float* scale, int64_t n) {
   if (i < n) scale[i] = scale_of_absmax(scale[i]);   // scale[i] holds the column max
 }
 
+// ---------------------------------------------------------------------------
+// cols, one kernel (rows <= 8192): a 1024-thread workgroup owns a band of BC
+// columns and every row, holding the band in registers (at most 32 floats
+// per thread), so X is read from HBM once.  The column maxima are reduced
+// inside the workgroup (lane shuffles, then LDS across the 16 waves), the
+// int8 values are written transposed into an LDS tile [BC][rows] and stored
+// as K-contiguous rows of Qt.  Bands that share a 128-byte line of X are
+// given to workgroups on the same XCD (ids are dealt to the 8 XCDs
+// round-robin), so the line is fetched into one L2 only.
+// ---------------------------------------------------------------------------
+constexpr int QCR_THREADS = 1024;
+constexpr int QCR_VPT = 8;            // float4 groups per thread
+constexpr int QCR_MAX_ELEMS = QCR_THREADS * QCR_VPT * 4;   // 32768 per band
+
+__device__ __forceinline__ int xcd_grouped(int wg, int total) {
+  const int xcd = wg & 7, idx = wg >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+template <int BC>
+__global__ void __launch_bounds__(QCR_THREADS)
+qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                 int8_t* __restrict__ Qt, int64_t ldqt, float* __restrict__ scale, int vec_in,
+                 int vec_out) {
+  constexpr int C4 = BC / 4;                 // threads per row
+  constexpr int RPP = QCR_THREADS / C4;      // rows per pass
+  constexpr int TILE = QCR_MAX_ELEMS;        // bytes of the transposed tile
+  __shared__ float red[QCR_THREADS / 64][BC];
+  __shared__ float s_inv[BC];
+  __shared__ __attribute__((aligned(16))) int8_t tile[TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t j0 = (int64_t)xcd_grouped(blockIdx.x, gridDim.x) * BC;
+  const int cg = tid % C4, r_off = tid / C4;
+  const int rp = (int)((rows + 15) / 16 * 16);     // tile row pitch (bytes per column)
+
+  float4 v[QCR_VPT];
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+#pragma unroll
+  for (int p = 0; p < QCR_VPT; ++p) {
+    const int64_t r = r_off + (int64_t)p * RPP;
+    v[p] = r < rows ? load4(X + r * ldx, j0 + cg * 4, cols, vec_in) : make_float4(0.f, 0.f, 0.f, 0.f);
+    m0 = fmaxf(m0, fabsf(v[p].x));
+    m1 = fmaxf(m1, fabsf(v[p].y));
+    m2 = fmaxf(m2, fabsf(v[p].z));
+    m3 = fmaxf(m3, fabsf(v[p].w));
+  }
+  // lanes l, l+C4, l+2*C4, ... of a wave hold the same columns
+#pragma unroll
+  for (int off = C4; off < 64; off <<= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+    m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+    m2 = fmaxf(m2, __shfl_xor(m2, off, 64));
+    m3 = fmaxf(m3, __shfl_xor(m3, off, 64));
+  }
+  if (lane < C4) {
+    red[wave][cg * 4 + 0] = m0;
+    red[wave][cg * 4 + 1] = m1;
+    red[wave][cg * 4 + 2] = m2;
+    red[wave][cg * 4 + 3] = m3;
+  }
+  __syncthreads();
+  if (tid < BC) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < QCR_THREADS / 64; ++w) a = fmaxf(a, red[w][tid]);
+    const float s = scale_of_absmax(a);
+    s_inv[tid] = recip_rn(s);
+    if (j0 + tid < cols) scale[j0 + tid] = s;
+  }
+  __syncthreads();
+  const float i0 = s_inv[cg * 4], i1 = s_inv[cg * 4 + 1], i2 = s_inv[cg * 4 + 2], i3 = s_inv[cg * 4 + 3];
+#pragma unroll
+  for (int p = 0; p < QCR_VPT; ++p) {
+    const int r = r_off + p * RPP;
+    if (r < rows) {
+      tile[(cg * 4 + 0) * rp + r] = (int8_t)quantize1(v[p].x, i0);
+      tile[(cg * 4 + 1) * rp + r] = (int8_t)quantize1(v[p].y, i1);
+      tile[(cg * 4 + 2) * rp + r] = (int8_t)quantize1(v[p].z, i2);
+      tile[(cg * 4 + 3) * rp + r] = (int8_t)quantize1(v[p].w, i3);
+    }
+  }
+  __syncthreads();
+  // store: BC rows of Qt, rows bytes each, 16 bytes per thread
+  const int r16 = rp / 16;
+  for (int q = tid; q < BC * r16; q += QCR_THREADS) {
+    const int c = q / r16, off = (q % r16) * 16;
+    const int64_t j = j0 + c;
+    if (j >= cols) continue;
+    int8_t* dst = Qt + j * ldqt + off;
+    const int8_t* src = tile + c * rp + off;
+    if (vec_out && off + 16 <= rows) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    } else {
+      for (int e = 0; e < 16 && off + e < rows; ++e) dst[e] = src[e];
+    }
+  }
+}
+
+// Band width for the one-kernel path: as wide as the registers allow (BC *
+// rows <= 32768) while leaving at least 128 workgroups; 0 = use the
+// multi-kernel path (more than 8192 rows).
+static int qcols_band(int64_t rows, int64_t cols) {
+  if (rows > QCR_MAX_ELEMS / 4) return 0;
+  int bc = 4;
+  for (int c = 64; c >= 4; c >>= 1) {
+    if ((int64_t)c * rows > QCR_MAX_ELEMS) continue;
+    bc = c;
+    if ((cols + c - 1) / c >= 128) break;
+  }
+  return bc;
+}
+
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                 int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Qt % 16 == 0) && (ldqt % 16 == 0);
+  const int bc = rows > 0 ? qcols_band(rows, cols) : 0;
+  if (bc > 0) {
+    const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
+    switch (bc) {
+      case 64: hipLaunchKernelGGL(qcols_reg_kernel<64>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 32: hipLaunchKernelGGL(qcols_reg_kernel<32>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 16: hipLaunchKernelGGL(qcols_reg_kernel<16>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 8: hipLaunchKernelGGL(qcols_reg_kernel<8>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      default: hipLaunchKernelGGL(qcols_reg_kernel<4>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+    }
+    return hipGetLastError();
+  }
   unsigned int* maxbits = reinterpret_cast<unsigned int*>(scale);
   hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
                      stream, maxbits, cols);

@@ -120,7 +120,8 @@ def test_quantize_rows_unaligned(g):
     assert_bits(s.cpu().numpy(), so, "scale")
 
 
-QC_SHAPES = [(1, 1), (5, 3), (300, 17), (768, 64), (1000, 100), (130, 257), (3072, 40), (65, 1030)]
+QC_SHAPES = [(1, 1), (5, 3), (300, 17), (768, 64), (1000, 100), (130, 257), (3072, 40), (65, 1030),
+             (512, 300), (8192, 70), (8193, 33), (2, 5000)]
 
 
 @pytest.mark.parametrize("rows,cols", QC_SHAPES)
