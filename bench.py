@@ -218,6 +218,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "w1"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="also run one plain device copy of MB MiB (a reference for HBM "
+                         "byte counters collected by a profiler around this run)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
@@ -232,6 +235,13 @@ def main():
     log(f"[bench] workload {a.workload}: generating inputs")
     desc, tensors, gemms = make_workload(a.workload)
     step = GpuStep(g, torch, tensors, gemms)
+    if a.copy_probe > 0:
+        src = torch.ones(a.copy_probe << 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {a.copy_probe} MiB read + {a.copy_probe} MiB written")
+        del src, dst
     ops = sum(2.0 * e["M"] * e["N"] * e["K"] for e in step.gemms)
     log(f"[bench] {len(step.gemms)} GEMMs, {ops / 1e9:.2f} GOP per step; warmup {a.warmup}")
     for _ in range(a.warmup):

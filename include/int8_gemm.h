@@ -43,7 +43,7 @@
  *   - The library allocates no device memory.  Calls that share a
  *     workspace must be ordered (same stream, or synchronized).
  *   - No kernel waits on another workgroup and no call synchronizes with
- *     the host.
+ *     the host: grid-wide sums end in the workgroup that finishes last.
  */
 #ifndef INT8_GEMM_H
 #define INT8_GEMM_H
@@ -116,9 +116,12 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
  *          ignored): receives output_hash(C) for this output.
  *   workspace, workspace_bytes
  *          device scratch of at least gemm_i8_workspace_bytes(M, N, K)
- *          bytes, 256-byte aligned, with any contents (nothing needs to be
- *          initialized; the call overwrites what it uses: per-tile shares
- *          of the hash and, when K is split, int32 partial sums).
+ *          bytes, 256-byte aligned.  Its first 256 bytes (a control
+ *          header: the hash's share counter) must be zero before the first
+ *          call that uses it; every call leaves them zero again, so one
+ *          zeroed buffer serves any sequence of ordered calls.  The rest is
+ *          scratch with any contents (per-tile shares of the hash, and with
+ *          a split K the int32 partial sums).
  * acc[i,j] = sum_k QA[i,k]*QBt[j,k] is exact (int32); the K range may be
  * split across workgroups, which cannot change a byte since integer
  * addition is associative.
@@ -138,7 +141,7 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row,
 /* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256). */
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* Bytes of workspace output_hash needs (a constant, 16 KiB). */
+/* Bytes of workspace output_hash needs (a constant, 256 + 16 KiB). */
 size_t output_hash_workspace_bytes(void);
 
 /*
@@ -154,9 +157,10 @@ size_t output_hash_workspace_bytes(void);
  *   C      M x N f32, leading dimension ldc >= N; M, N < 2^31.
  *   hash   device pointer to one uint64_t that receives H.
  *   workspace  device scratch of output_hash_workspace_bytes() bytes,
- *          256-byte aligned, any contents.
- * The sum is taken modulo 2^64, so it is reduced in any order (per-
- * workgroup shares, then one add-up), with no atomics.
+ *          256-byte aligned, with the same 256-byte zero header as the
+ *          GEMM's workspace (one zeroed buffer may serve both calls).
+ * The sum is taken modulo 2^64, so it is reduced in any order: each
+ * workgroup writes its share, and the last one to finish adds them up.
  * Errors: I8G_EINVAL, I8G_EWORKSPACE, I8G_EHIP.
  */
 int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,

@@ -140,13 +140,14 @@ def workspace_bytes(M, N, K):
 
 
 def _workspace(device, nbytes):
-    """Scratch buffer per (device, stream), grown on demand; the library
-    needs no particular contents in it."""
+    """Scratch buffer per (device, stream), grown on demand.  It is zeroed
+    when allocated: the library needs its 256-byte header zero and leaves
+    it zero after every call."""
     key = (device.index if device.index is not None else torch.cuda.current_device(),
            torch.cuda.current_stream(device).cuda_stream)
     ws = _ws.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws[key] = ws
     return ws
 

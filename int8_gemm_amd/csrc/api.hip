@@ -66,7 +66,7 @@ size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return plan.workspace_bytes > 256 ? plan.workspace_bytes : 256;
 }
 
-size_t output_hash_workspace_bytes(void) { return (size_t)kHashMaxParts * 8; }
+size_t output_hash_workspace_bytes(void) { return kWsHeader + (size_t)kHashMaxParts * 8; }
 
 int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,
                         int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K, float* C,
@@ -80,10 +80,8 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
   if (K > I8G_K_MAX) return I8G_EKRANGE;
   if (!workspace || ((uintptr_t)workspace % 256) != 0) return I8G_EWORKSPACE;
   if (M == 0 || N == 0) {
-    if (workspace_bytes < 256) return I8G_EWORKSPACE;
-    if (want_hash)
-      return hip_status(launch_hash_finalize(reinterpret_cast<unsigned long long*>(workspace), 0, M,
-                                             N, hash, as_stream(stream)));
+    if (workspace_bytes < kWsHeader) return I8G_EWORKSPACE;
+    if (want_hash) return hip_status(launch_output_hash(C, M, N, ldc, hash, workspace, as_stream(stream)));
     return I8G_OK;
   }
   if (!C || !s_row || !s_col || ldc < N) return I8G_EINVAL;
@@ -116,7 +114,9 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
   p.do_hash = want_hash ? 1 : 0;
   p.stream_out = ((double)M * (double)N * 4.0 > 128.0 * 1024 * 1024) ? 1 : 0;
   char* ws = reinterpret_cast<char*>(workspace);
-  p.hash_parts = reinterpret_cast<unsigned long long*>(ws);
+  p.ticket = reinterpret_cast<unsigned int*>(ws);
+  p.hash_parts = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
+  p.n_shares = plan.hash_parts;
   p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
   p.hash_out = hash;
   return hip_status(launch_gemm(p, plan, as_stream(stream)));
@@ -129,9 +129,7 @@ int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* has
   if (!workspace || ((uintptr_t)workspace % 256) != 0 ||
       workspace_bytes < output_hash_workspace_bytes())
     return I8G_EWORKSPACE;
-  return hip_status(launch_output_hash(C, M, N, ldc, hash,
-                                       reinterpret_cast<unsigned long long*>(workspace),
-                                       as_stream(stream)));
+  return hip_status(launch_output_hash(C, M, N, ldc, hash, workspace, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -26,8 +26,8 @@
 //  * The epilogue converts, scales (row scale, then column scale, separate
 //    roundings), applies ReLU as a select (so never -0), stores f32, and
 //    computes the tile's share of the output hash S = sum c(j)*r(i)*bits(i,j)
-//    mod 2^64, stored in a per-tile slot; a one-workgroup kernel adds the
-//    slots (mod 2^64, any order) and writes H.
+//    mod 2^64; the workgroup that finishes last adds the shares (mod 2^64,
+//    any order) and writes H (see hash_share_and_finalize).
 #include <cmath>
 #include <cstdlib>
 
@@ -138,13 +138,14 @@ __device__ __forceinline__ void store_out4(float* dst, float a, float b, float c
 }
 
 // Epilogue through LDS.  Each wave parks its raw int32 accumulators 32 rows
-// at a time in a private LDS slab (MFMA layout: lane = one column, 16 rows;
-// row stride WTN+8 words, so the two half-waves' rows land on disjoint
-// banks), reads the slab back row-major with 4 consecutive columns per lane,
-// and only then applies y = RN(RN(RN(acc) * s_row) * s_col), the ReLU select
-// and the hash terms r(i)*bits(y), summed per column; each lane writes 16
-// bytes per row so the lanes cover whole row segments.  With split-K the raw
-// sums are written the same way to the split's partial plane.
+// at a time in a private LDS slab (MFMA layout written: lane = one column,
+// 16 rows; row stride WTN+8 words, so the two half-waves' rows land on
+// disjoint banks), reads the slab back row-major, 4 consecutive columns per
+// lane, computes y = RN(RN(RN(acc) * s_row) * s_col), the ReLU select and
+// the hash terms r(i)*bits(y) (summed per column), and writes 16 bytes per
+// lane per row, so the lanes cover whole row segments.  The workgroup's
+// share of S is published last (hash_share_and_finalize).  With split-K the
+// raw int32 sums are stored instead, to the split's plane.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM][FN], int8_t* smem,
                                              int tm, int tn, int split) {
@@ -166,7 +167,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   int* slab = reinterpret_cast<int*>(smem) + wave * SLAB;
   float* s_sr = reinterpret_cast<float*>(smem) + NWAVES * SLAB;
   unsigned int* s_rk = reinterpret_cast<unsigned int*>(s_sr + BM);
-  unsigned long long* s_red = reinterpret_cast<unsigned long long*>(s_rk + BM);
+  unsigned long long* s_red = reinterpret_cast<unsigned long long*>(s_rk + BM);   // NWAVES + 1 words
   // row scales and row keys of the tile (zero beyond M: such rows add nothing)
   for (int r = tid; r < BM; r += NT) {
     const int gr = tm * BM + r;
@@ -177,25 +178,29 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   const int rr0 = lane / LPR, cc = (lane % LPR) * 4;
   const int gc0 = col0 + cc;
   float sc[4];
-  uint64_t tcol[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 4; ++e) sc[e] = gc0 + e < N ? p.s_col[gc0 + e] : 0.0f;
   __syncthreads();
 
-  const int64_t ld = raw ? (int64_t)N : p.ldc;
-  const bool vec = raw ? (N % 4 == 0) : ((p.ldc % 4 == 0) && (((uintptr_t)p.C & 15) == 0));
-  int* part_base = raw ? p.partials + (int64_t)split * M * N : nullptr;
-
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  // slab i of this wave: park the accumulators, then visit its rows
+  // row-major; the slab is private to the wave and LDS operations of a wave
+  // complete in order, so no barrier is needed between the two
+  auto park = [&](int i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int srow = (v >> 2) * 8 + lhalf * 4 + (v & 3);
 #pragma unroll
       for (int j = 0; j < FN; ++j) slab[srow * STRIDE + j * 32 + lrow] = acc[i][j][v];
     }
-    // the slab is private to this wave and LDS operations of a wave complete
-    // in order, so it can be read back without a barrier
+  };
+
+  uint64_t tcol[4] = {0, 0, 0, 0};
+  const int64_t ld = raw ? (int64_t)N : p.ldc;
+  const bool vec = raw ? (N % 4 == 0) : ((p.ldc % 4 == 0) && (((uintptr_t)p.C & 15) == 0));
+  int* part_base = raw ? p.partials + (int64_t)split * M * N : nullptr;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    park(i);
 #pragma unroll
     for (int t = 0; t < 32 / RPI; ++t) {
       const int srow = t * RPI + rr0;
@@ -204,15 +209,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
       const int gr = tm * BM + lr;
       const int av[4] = {a.x, a.y, a.z, a.w};
       if (raw) {
-        if (gr < M) {
-          int* dst = part_base + (int64_t)gr * ld + gc0;
-          if (vec && gc0 + 4 <= N) {
-            *reinterpret_cast<int4*>(dst) = a;
-          } else {
+        if (gr >= M) continue;
+        int* dst = part_base + (int64_t)gr * ld + gc0;
+        if (vec && gc0 + 4 <= N) {
+          *reinterpret_cast<int4*>(dst) = a;
+        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gc0 + e < N) dst[e] = av[e];
-          }
+          for (int e = 0; e < 4; ++e)
+            if (gc0 + e < N) dst[e] = av[e];
         }
       } else {
         const float sr = s_sr[lr];
@@ -224,15 +228,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
           if (relu) y[e] = relu_pos0(y[e]);
           tcol[e] += rk * (uint64_t)__float_as_uint(y[e]);
         }
-        if (gr < M) {
-          float* dst = p.C + (int64_t)gr * ld + gc0;
-          if (vec && gc0 + 4 <= N) {
-            store_out4(dst, y[0], y[1], y[2], y[3], stream);
-          } else {
+        if (gr >= M) continue;
+        float* dst = p.C + (int64_t)gr * ld + gc0;
+        if (vec && gc0 + 4 <= N) {
+          store_out4(dst, y[0], y[1], y[2], y[3], stream);
+        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gc0 + e < N) dst[e] = y[e];
-          }
+          for (int e = 0; e < 4; ++e)
+            if (gc0 + e < N) dst[e] = y[e];
         }
       }
     }
@@ -243,7 +246,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
     for (int e = 0; e < 4; ++e)
       if (gc0 + e < N) hsum += hash_col_key((uint64_t)(gc0 + e)) * tcol[e];
     const uint64_t part = block_sum_u64<NT>(hsum, s_red);
-    if (tid == 0) p.hash_parts[tm * p.tiles_n + tn] = part;
+    hash_share_and_finalize<NT>(part, p.hash_parts, p.ticket, p.n_shares, tm * p.tiles_n + tn,
+                                (uint64_t)M, (uint64_t)N, p.hash_out, s_red,
+                                reinterpret_cast<int*>(s_red + NWAVES));
   }
 }
 
@@ -430,6 +435,7 @@ constexpr int COMB_ROWS = 32;
 __global__ void __launch_bounds__(256)
 splitk_combine_kernel(const GemmParams p) {
   __shared__ unsigned long long red[4];
+  __shared__ int last_flag;
   const int M = p.M, N = p.N;
   const int tid = threadIdx.x;
   const int c0 = (blockIdx.x * 256 + tid) * 4;
@@ -479,26 +485,12 @@ splitk_combine_kernel(const GemmParams p) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     if (c0 + e < N) part += hash_col_key((uint64_t)(c0 + e)) * t[e];
-  part = block_sum_u64<256>(part, red);
-  if (p.do_hash && tid == 0) p.hash_parts[blockIdx.y * gridDim.x + blockIdx.x] = part;
-}
-
-// H = fmix64(sum of the shares ^ fmix64(M*2^32 + N)), one workgroup.
-__global__ void __launch_bounds__(256)
-hash_finalize_kernel(const unsigned long long* parts, int n, uint64_t M, uint64_t N,
-                     uint64_t* hash_out) {
-  __shared__ unsigned long long red[4];
-  uint64_t s = 0;
-  for (int i = threadIdx.x; i < n; i += 256) s += parts[i];
-  s = block_sum_u64<256>(s, red);
-  if (threadIdx.x == 0) *hash_out = hash_finalize(s, M, N);
-}
-
-hipError_t launch_hash_finalize(const unsigned long long* parts, int n, int64_t M, int64_t N,
-                                uint64_t* hash_out, hipStream_t stream) {
-  hipLaunchKernelGGL(hash_finalize_kernel, dim3(1), dim3(256), 0, stream, parts, n, (uint64_t)M,
-                     (uint64_t)N, hash_out);
-  return hipGetLastError();
+  if (p.do_hash) {
+    part = block_sum_u64<256>(part, red);
+    hash_share_and_finalize<256>(part, p.hash_parts, p.ticket, p.n_shares,
+                                 blockIdx.y * gridDim.x + blockIdx.x, (uint64_t)M, (uint64_t)N,
+                                 p.hash_out, red, &last_flag);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -586,7 +578,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   } else {
     best.hash_parts = (int)tiles;
   }
-  size_t bytes = ((size_t)best.hash_parts * 8 + 255) / 256 * 256;
+  size_t bytes = kWsHeader + ((size_t)best.hash_parts * 8 + 255) / 256 * 256;
   best.partials_offset = bytes;
   if (best.splits > 1) bytes += (size_t)best.splits * M * N * 4;
   best.workspace_bytes = bytes;
@@ -611,8 +603,6 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
   }
   if (plan.splits > 1)
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(plan.comb_x, plan.comb_y), dim3(256), 0, stream, p);
-  if (p.do_hash)
-    return launch_hash_finalize(p.hash_parts, plan.hash_parts, p.M, p.N, p.hash_out, stream);
   return hipGetLastError();
 }
 

@@ -8,8 +8,8 @@
 // HBM-bound: each thread owns 4 consecutive columns and walks bands of rows
 // (grid-stride, at most kHashMaxParts workgroups), summing r(i)*bits with
 // one 32x32->64 multiply-add per element and multiplying by the column keys
-// once; each workgroup stores its share of S in a slot, and a one-workgroup
-// kernel adds the shares (integer sums: no order dependence, no atomics).
+// once; the workgroup that finishes last adds the workgroups' shares of S
+// (integer sums: no order dependence) and writes H.
 #include "i8g_device.h"
 #include "i8g_launch.h"
 
@@ -19,8 +19,9 @@ constexpr int HASH_ROWS = 32;     // rows per band
 
 __global__ void __launch_bounds__(256)
 output_hash_kernel(const float* __restrict__ C, int64_t M, int64_t N, int64_t ldc, int vec_in,
-                   unsigned long long* parts) {
+                   unsigned long long* parts, unsigned int* ticket, uint64_t* hash_out) {
   __shared__ unsigned long long red[4];
+  __shared__ int last_flag;
   const int tid = threadIdx.x;
   uint64_t part = 0;
   for (int64_t c = ((int64_t)blockIdx.x * 256 + tid) * 4; c < N; c += (int64_t)gridDim.x * 1024) {
@@ -50,20 +51,33 @@ output_hash_kernel(const float* __restrict__ C, int64_t M, int64_t N, int64_t ld
     if (c + 3 < N) part += hash_col_key((uint64_t)c + 3) * t3;
   }
   part = block_sum_u64<256>(part, red);
-  if (tid == 0) parts[blockIdx.y * gridDim.x + blockIdx.x] = part;
+  hash_share_and_finalize<256>(part, parts, ticket, gridDim.x * gridDim.y,
+                               blockIdx.y * gridDim.x + blockIdx.x, (uint64_t)M, (uint64_t)N,
+                               hash_out, red, &last_flag);
+}
+
+__global__ void empty_hash_kernel(uint64_t* hash_out, uint64_t M, uint64_t N) {
+  if (threadIdx.x == 0) *hash_out = hash_finalize(0, M, N);
 }
 
 hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* hash,
-                              unsigned long long* parts, hipStream_t stream) {
-  if (M == 0 || N == 0) return launch_hash_finalize(parts, 0, M, N, hash, stream);
+                              void* workspace, hipStream_t stream) {
+  if (M == 0 || N == 0) {
+    hipLaunchKernelGGL(empty_hash_kernel, dim3(1), dim3(64), 0, stream, hash, (uint64_t)M, (uint64_t)N);
+    return hipGetLastError();
+  }
+  unsigned int* ticket = reinterpret_cast<unsigned int*>(workspace);
+  unsigned long long* parts =
+      reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(workspace) + kWsHeader);
   const int vec_in = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
   int64_t gx = (N + 1023) / 1024;
   if (gx > kHashMaxParts) gx = kHashMaxParts;   // columns beyond: grid-stride
   int64_t gy = (M + HASH_ROWS - 1) / HASH_ROWS;
   if (gx * gy > kHashMaxParts) gy = kHashMaxParts / gx;   // rows beyond: grid-stride
   const dim3 grid((unsigned int)gx, (unsigned int)gy);
-  hipLaunchKernelGGL(output_hash_kernel, grid, dim3(256), 0, stream, C, M, N, ldc, vec_in, parts);
-  return launch_hash_finalize(parts, (int)(gx * gy), M, N, hash, stream);
+  hipLaunchKernelGGL(output_hash_kernel, grid, dim3(256), 0, stream, C, M, N, ldc, vec_in, parts,
+                     ticket, hash);
+  return hipGetLastError();
 }
 
 }  // namespace i8g

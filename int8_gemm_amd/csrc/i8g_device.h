@@ -126,4 +126,44 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, unsigned long long
   return t;
 }
 
+// Ends a grid-wide sum of per-workgroup hash shares without a second kernel
+// and without agent-scope release/acquire fences (on this GPU those write
+// back / invalidate the whole L2 of the XCD).  Every workgroup stores its
+// share with an agent-scope atomic store (written through to the coherence
+// point), waits for that store to be acknowledged (s_waitcnt vmcnt(0); a
+// workgroup-scope fence alone emits no wait for global stores here), then
+// takes a ticket with an agent-scope atomic add.  The workgroup that draws the last ticket knows
+// every other share was complete before its ticket was taken; it reads the
+// shares with agent-scope atomic loads, writes H, and returns the ticket to
+// zero for the next call.  `ticket` must be zero when the grid starts.
+// Call from all NT threads of every workgroup; `part` is valid in thread 0.
+template <int NT>
+__device__ __forceinline__ void hash_share_and_finalize(uint64_t part, unsigned long long* shares,
+                                                        unsigned int* ticket, int n_shares,
+                                                        int my_share, uint64_t M, uint64_t N,
+                                                        uint64_t* hash_out,
+                                                        unsigned long long* red, int* flag) {
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(shares + my_share, (unsigned long long)part, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // keeps the compiler's order
+    __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): the store is acknowledged
+    const unsigned int t =
+        __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (t == (unsigned int)(n_shares - 1));
+  }
+  __syncthreads();
+  if (*flag) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    uint64_t s = 0;
+    for (int i = threadIdx.x; i < n_shares; i += NT)
+      s += __hip_atomic_load(shares + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s = block_sum_u64<NT>(s, red);
+    if (threadIdx.x == 0) {
+      *hash_out = hash_finalize(s, M, N);
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 }  // namespace i8g

@@ -19,6 +19,8 @@ struct GemmParams {
   int relu, do_hash;
   int stream_out;                   // store C with nontemporal hints (large outputs)
   unsigned long long* hash_parts;   // per-tile (or per-combine-group) shares of S
+  unsigned int* ticket;             // workspace word counting finished shares (zero between calls)
+  int n_shares;                     // shares of S written by the kernel that ends the call
   int* partials;                    // split-K int32 partial sums, [split][M][N]
   uint64_t* hash_out;
 };
@@ -43,11 +45,13 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                 int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream);
 hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
-                              uint64_t* hash, unsigned long long* parts, hipStream_t stream);
-hipError_t launch_hash_finalize(const unsigned long long* parts, int n, int64_t M, int64_t N,
-                                uint64_t* hash_out, hipStream_t stream);
+                              uint64_t* hash, void* workspace, hipStream_t stream);
 
-// output_hash uses at most this many shares (its workspace is 8 bytes each)
+// Workspace layout shared by every call: a 256-byte header (word 0 is the
+// share ticket, zero between calls), then 8-byte hash shares, then (GEMM
+// split-K only) int32 partial sums.
+constexpr size_t kWsHeader = 256;
+// output_hash uses at most this many shares
 constexpr int kHashMaxParts = 2048;
 
 }  // namespace i8g

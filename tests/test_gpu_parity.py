@@ -263,9 +263,10 @@ def test_error_statuses(g):
     assert rc == 1
 
 
-def test_workspace_contents_do_not_matter(g):
-    """The workspace is scratch: filling it with garbage before each call
-    changes no byte; repeated split-K calls give identical bytes."""
+def test_workspace_scratch_contents_do_not_matter(g):
+    """Beyond its 256-byte header the workspace is scratch: garbage there
+    changes no byte; the header is zero after every call; repeated split-K
+    calls give identical bytes and hashes."""
     say("workspace garbage")
     rng = np.random.default_rng(79)
     A = rng.standard_normal((700, 9000)).astype(F32)
@@ -273,7 +274,7 @@ def test_workspace_contents_do_not_matter(g):
     C, *_ = ref.blockscaled_gemm(A, B, False)
     for it in range(3):
         for ws in g._ws.values():
-            ws.random_(0, 256)
+            ws[256:].random_(0, 256)
         os.environ["I8G_FORCE_SPLITS"] = "3"
         try:
             got = run_method(g, A, B, relu=False)
@@ -281,6 +282,8 @@ def test_workspace_contents_do_not_matter(g):
             os.environ.pop("I8G_FORCE_SPLITS", None)
         assert_bits(got["C"], C, f"C call {it}")
         assert got["hash"] == hashref.output_hash(C)
+        for ws in g._ws.values():
+            assert int(torch.count_nonzero(ws[:256]).item()) == 0
 
 
 def test_metamorphic_on_gpu(g):
