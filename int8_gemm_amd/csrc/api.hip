@@ -62,8 +62,12 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_
 
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0) return 256;
-  GemmPlan plan = plan_gemm(M, N, K > 0 ? K : 1);
-  return plan.workspace_bytes > 256 ? plan.workspace_bytes : 256;
+  // the plan may depend on ldc (very wide rows exclude the persistent
+  // kernel): size for either
+  const GemmPlan a = plan_gemm(M, N, K > 0 ? K : 1, true);
+  const GemmPlan b = plan_gemm(M, N, K > 0 ? K : 1, false);
+  size_t bytes = a.workspace_bytes > b.workspace_bytes ? a.workspace_bytes : b.workspace_bytes;
+  return bytes > 256 ? bytes : 256;
 }
 
 size_t output_hash_workspace_bytes(void) { return kWsHeader + (size_t)kHashMaxParts * 8; }
@@ -92,7 +96,7 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
         ldb < k16)
       return I8G_EALIGN;
   }
-  GemmPlan plan = plan_gemm(M, N, K > 0 ? K : 1);
+  GemmPlan plan = plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc);
   if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
   GemmParams p;
   p.A = QA;

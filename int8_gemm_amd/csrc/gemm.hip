@@ -30,6 +30,7 @@
 //    any order) and writes H (see hash_share_and_finalize).
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "i8g_device.h"
 #include "i8g_launch.h"
@@ -425,6 +426,449 @@ gemm_i8_dma_kernel(const GemmParams p) {
   epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, tm, tn, split);
 }
 
+// Calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent GEMM with a drained epilogue.
+//
+// One workgroup per CU walks a sequence of output tiles.  Its four waves
+// (one per SIMD) keep two sets of accumulators: while the MFMAs of tile t
+// accumulate into one set, the epilogue of tile t-1 is computed from the
+// other set, one 32x32 block per K stage, and written with buffer stores
+// straight from the MFMA register layout (each store covers two 128-byte
+// row segments).  The epilogue's VALU work and its stores are thereby hidden
+// under matrix-core work instead of following it, which matters when the
+// f32 output write bounds the GEMM (K = 768).
+//
+// The ring of LDS stages runs across tile boundaries: near the end of a
+// tile, the stages of the next tile are already being fetched.  Waits on
+// the vector-memory counter count the epilogue's stores as well (gfx950
+// retires loads and stores in issue order for s_waitcnt vmcnt).
+//
+// Output masking: the buffer resource of a tile starts at the tile's first
+// row and has a large record count; a lane whose element lies outside the
+// matrix gets a voffset at or above that count, so the hardware drops the
+// store whether or not the scalar offset enters the range check.
+// Requires K % 64 == 0, K >= 64 * (STAGES - 1) and ldc <= kPersistMaxLdc (the
+// offsets within a 32-row block stay below the record count).
+// ---------------------------------------------------------------------------
+// A pointer the caller knows to be the same in every lane, in scalar
+// registers (a buffer resource built from it then needs no per-lane loop).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* q) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)q;
+}
+
+constexpr unsigned int kBufRecords = 0x7FFFFFF0u;   // record count of the output resource
+constexpr int kBufInvalid = 0x7FFFFFF0;             // voffset of a dropped store
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool RELU>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
+gemm_i8_persist_kernel(const GemmParams p) {
+  constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
+  static_assert(NWAVES == 4, "four waves, one per SIMD");
+  static_assert(STAGES >= 3, "the ring needs at least three stages");
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int FM = WTM / 32, FN = WTN / 32, NB = FM * FN;
+  constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  constexpr int A_INS = BM / (16 * NWAVES), B_INS = BN / (16 * NWAVES);
+  static_assert(A_INS * 16 * NWAVES == BM && B_INS * 16 * NWAVES == BN, "rows per stage");
+  constexpr int LPS = A_INS + B_INS;
+  constexpr int RING = STAGES * STAGE;
+  static_assert(LPS + 2 * 16 < 64, "vmcnt counts fit the 6-bit counter");
+  constexpr int SCL = BM + BN;                          // floats per scale slot: rows, then columns
+  constexpr int NSI = SCL / 64;                         // dword DMA instructions per slot
+  static_assert(NSI * 64 == SCL, "tile sides are multiples of 64");
+  constexpr int SQ = (NSI + NWAVES - 1) / NWAVES;       // per wave (at most)
+  __shared__ __attribute__((aligned(1024))) int8_t smem[RING + 3 * SCL * 4 + 3 * BM * 4 + 64];
+  // three slots: tile r's scales and row keys live in slot r % 3 from the
+  // time its first stage is fetched until its epilogue is drained
+  float* const s_scl = reinterpret_cast<float*>(smem + RING);                              // [3][SCL]
+  unsigned int* const s_rk = reinterpret_cast<unsigned int*>(smem + RING + 3 * SCL * 4);  // [3][BM]
+  unsigned long long* const s_red =
+      reinterpret_cast<unsigned long long*>(smem + RING + 3 * SCL * 4 + 3 * BM * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int M = p.M, N = p.N;
+  const int nst = p.K / BK;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int G = gridDim.x;
+  const int64_t ldc4 = p.ldc * 4;
+
+  // This workgroup's place in the tile sequence: workgroups are dealt to
+  // the 8 XCDs round-robin; in each round the XCDs take consecutive chunks
+  // of the L2-grouped tile order.
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int per = G >> 3, rem = G & 7;
+  const int wpos = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int my_tiles = wpos < tiles ? (tiles - 1 - wpos) / G + 1 : 0;
+  auto tile_coords = [&](int r, int& tm, int& tn) __attribute__((always_inline)) {
+    const int n = r * G + wpos;
+    const int group_size = GROUP_M * p.tiles_n;
+    const int group = n / group_size;
+    const int first_m = group * GROUP_M;
+    const int gm = (p.tiles_m - first_m) < GROUP_M ? (p.tiles_m - first_m) : GROUP_M;
+    const int in_group = n - group * group_size;
+    tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
+    tn = __builtin_amdgcn_readfirstlane(in_group / gm);
+  };
+
+  // ---- direct-to-LDS loads of one stage (see gemm_i8_dma_kernel) ----
+  const int r_in = lane >> 2, slot = lane & 3;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copies
+  const int wm_s = wave_s / WAVES_N;
+  // Per tile: wave-uniform base addresses (scalar registers) and this
+  // lane's 32-bit offsets from them (rows clamped into the matrix).
+  struct Src {
+    const int8_t* abase;   // A at the tile's first row
+    const int8_t* bbase;   // B at the tile's first row
+    const float* rbase;    // s_row at the tile's first row
+    const float* cbase;    // s_col at the tile's first column
+    int a[A_INS];
+    int b[B_INS];
+    int sp[SQ];            // offset (floats) of this lane's scale, rows then columns
+    int slot;              // scale slot of the tile
+  };
+  auto make_src = [&](int r, int tm, int tn, Src& s) __attribute__((always_inline)) {
+    s.slot = __builtin_amdgcn_readfirstlane(r % 3);
+    const int row0 = tm * BM, col0 = tn * BN;
+    s.abase = uniform_ptr(p.A + (int64_t)row0 * p.lda);
+    s.bbase = uniform_ptr(p.B + (int64_t)col0 * p.ldb);
+    s.rbase = uniform_ptr(p.s_row + row0);
+    s.cbase = uniform_ptr(p.s_col + col0);
+#pragma unroll
+    for (int q = 0; q < SQ; ++q) {
+      const int e = (q * NWAVES + wave) * 64 + lane;   // index into [rows | columns]
+      if (e < BM) {
+        const int lr = e < M - row0 ? e : M - 1 - row0;
+        s.sp[q] = lr;
+      } else {
+        const int lc = (e - BM) < N - col0 ? (e - BM) : N - 1 - col0;
+        s.sp[q] = BM + lc;   // marks a column entry; see issue()
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < A_INS; ++q) {
+      const int row = (q * NWAVES + wave) * 16 + r_in;
+      const int lr = row < M - row0 ? row : M - 1 - row0;
+      s.a[q] = lr * (int)p.lda + (swz(row, slot) << 4);
+    }
+#pragma unroll
+    for (int q = 0; q < B_INS; ++q) {
+      const int row = (q * NWAVES + wave) * 16 + r_in;
+      const int lr = row < N - col0 ? row : N - 1 - col0;
+      s.b[q] = lr * (int)p.ldb + (swz(row, slot) << 4);
+    }
+  };
+  auto issue = [&](int buf, const Src& s, int kt) __attribute__((always_inline)) {
+    int8_t* base = smem + buf * STAGE + wave_s * 1024;
+    const int8_t* ab = s.abase + kt * BK;
+    const int8_t* bb = s.bbase + kt * BK;
+#pragma unroll
+    for (int q = 0; q < A_INS; ++q) dma_load16(ab + s.a[q], base + q * NWAVES * 1024);
+#pragma unroll
+    for (int q = 0; q < B_INS; ++q) dma_load16(bb + s.b[q], base + A_BYTES + q * NWAVES * 1024);
+    if (kt == 0) {
+      // the tile's row and column scales ride with its first stage; these
+      // extra loads only lengthen the queue that later waits count
+      float* sbase = s_scl + s.slot * SCL + wave_s * 64;
+#pragma unroll
+      for (int q = 0; q < SQ; ++q)
+        if (q * NWAVES + wave_s < NSI) {
+          const float* src = (q * NWAVES + wave_s) * 64 < BM ? s.rbase + s.sp[q] : s.cbase + (s.sp[q] - BM);
+          __builtin_amdgcn_global_load_lds(src, sbase + q * NWAVES * 64, 4, 0, 0);
+        }
+    }
+  };
+
+  // ---- fragments and MFMAs ----
+  int offa[2][FM], offb[2][FN];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * WTM + i * 32 + lrow;
+      offa[s][i] = row * BK + (swz(row, s * 2 + lhalf) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WTN + j * 32 + lrow;
+      offb[s][j] = A_BYTES + row * BK + (swz(row, s * 2 + lhalf) << 4);
+    }
+  }
+  v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto load_frags = [&](int buf, int s, v4i (&fa)[FM], v4i (&fb)[FN]) __attribute__((always_inline)) {
+    const int8_t* sb = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const v4i*>(sb + offa[s][i]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const v4i*>(sb + offb[s][j]);
+  };
+  v16i acc0[FM][FN], acc1[FM][FN];
+
+  // ---- epilogue state of the tile being drained ----
+  struct Out {
+    float* cbase;                  // C at the tile's first row
+    int voff[FN];                  // this lane's column (and half-wave row offset), or kBufInvalid
+    uint64_t ckey[FN];             // column hash keys (0 beyond N)
+    int rows_valid;                // rows of the tile inside the matrix
+    int slot;                      // scale / key slot of the tile
+  };
+  uint64_t tcol[FN];               // per-column hash sums of the tile being drained
+  uint64_t lane_hash = 0;          // this lane's share of S over every drained tile
+  auto make_out = [&](int r, int tm, int tn, Out& o) __attribute__((always_inline)) {
+    const int row0 = tm * BM;
+    o.cbase = uniform_ptr(p.C + (int64_t)row0 * p.ldc);
+    o.rows_valid = __builtin_amdgcn_readfirstlane((M - row0) < BM ? (M - row0) : BM);
+    o.slot = __builtin_amdgcn_readfirstlane(r % 3);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = tn * BN + wn * WTN + j * 32 + lrow;
+      const bool ok = col < N;
+      o.voff[j] = ok ? (int)(lhalf * 4 * ldc4 + col * 4) : kBufInvalid;
+      o.ckey[j] = ok ? hash_col_key((uint64_t)col) : 0ull;
+    }
+    // row hash keys of the tile (0 beyond M: those rows add nothing)
+    for (int rr = tid; rr < BM; rr += NT) {
+      const int gr = row0 + rr;
+      s_rk[o.slot * BM + rr] = gr < M ? hash_row_key((unsigned int)gr) : 0u;
+    }
+  };
+
+  // Drain block b = (i, j) of accumulator set `acc`: epilogue, ReLU, hash
+  // terms and 16 stores.  Rows of lane l, register v: (v/4)*8 + 4*(l/32) + v%4
+  // within the 32x32 block; column l%32.
+  auto drain_block = [&](v16i (&acc)[FM][FN], const Out& o, auto IJ) __attribute__((always_inline)) {
+    constexpr int b = decltype(IJ)::value;
+    constexpr int i = b / FN, j = b % FN;
+    const int rb = wm * WTM + i * 32 + lhalf * 4;             // this lane's first row in the tile
+    // Scales (landed by direct-to-LDS loads that earlier waits covered) and
+    // row keys, read with explicit LDS instructions: the compiler would
+    // otherwise wait for every outstanding direct-to-LDS load first.
+    v4i srq[4], rkq[4];
+    int scb;
+    {
+      const uint32_t sa = lds_addr(s_scl + o.slot * SCL + rb);
+      const uint32_t ka = lds_addr(s_rk + o.slot * BM + rb);
+      const uint32_t ca = lds_addr(s_scl + o.slot * SCL + BM + wn * WTN + j * 32 + lrow);
+      asm volatile("ds_read_b128 %0, %1" : "=v"(srq[0]) : "v"(sa));
+      asm volatile("ds_read_b128 %0, %1 offset:32" : "=v"(srq[1]) : "v"(sa));
+      asm volatile("ds_read_b128 %0, %1 offset:64" : "=v"(srq[2]) : "v"(sa));
+      asm volatile("ds_read_b128 %0, %1 offset:96" : "=v"(srq[3]) : "v"(sa));
+      asm volatile("ds_read_b128 %0, %1" : "=v"(rkq[0]) : "v"(ka));
+      asm volatile("ds_read_b128 %0, %1 offset:32" : "=v"(rkq[1]) : "v"(ka));
+      asm volatile("ds_read_b128 %0, %1 offset:64" : "=v"(rkq[2]) : "v"(ka));
+      asm volatile("ds_read_b128 %0, %1 offset:96" : "=v"(rkq[3]) : "v"(ka));
+      asm volatile("ds_read_b32 %0, %1" : "=v"(scb) : "v"(ca));
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(srq[0]), "+v"(srq[1]), "+v"(srq[2]), "+v"(srq[3]), "+v"(rkq[0]),
+                     "+v"(rkq[1]), "+v"(rkq[2]), "+v"(rkq[3]), "+v"(scb));
+    }
+    const float sc = __int_as_float(scb);
+    // rows of this 32-row block that lie inside the matrix (wave-uniform)
+    const int lim_w = o.rows_valid - (wm_s * WTM + i * 32);
+    // resource based at the block's first row: offsets stay below 32 rows
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(o.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
+        0x00020000);
+    auto body = [&](auto RAGGED) __attribute__((always_inline)) {
+      constexpr bool R = decltype(RAGGED)::value;
+      const int lim = lim_w - lhalf * 4;   // this lane's rows q*8+e below lim are inside
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float srs[4] = {__int_as_float(srq[q][0]), __int_as_float(srq[q][1]),
+                              __int_as_float(srq[q][2]), __int_as_float(srq[q][3])};
+        const unsigned int rks[4] = {(unsigned int)rkq[q][0], (unsigned int)rkq[q][1],
+                                     (unsigned int)rkq[q][2], (unsigned int)rkq[q][3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = q * 4 + e;
+          float y = epilogue1(acc[i][j][v], srs[e], sc);
+          if (RELU) y = relu_pos0(y);
+          tcol[j] += (uint64_t)rks[e] * (uint64_t)__float_as_uint(y);
+          const int soff = (q * 8 + e) * (int)ldc4;
+          int vo = o.voff[j];
+          if (R) vo = (q * 8 + e) < lim ? vo : kBufInvalid;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, vo, soff, 0);
+        }
+      }
+    };
+    if (lim_w >= 32) body(std::false_type());
+    else body(std::true_type());
+  };
+  auto close_tile_hash = [&](const Out& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      lane_hash += o.ckey[j] * tcol[j];
+      tcol[j] = 0;
+    }
+  };
+
+  // ---- one K stage of tile r (s = 0..nst-1) into accumulator set X ----
+  // g = global stage index of this workgroup (r*nst + s); gtotal = stages in
+  // all its tiles.  Fragments of k-step 0 of this stage are in fa0/fb0.
+  const int gtotal = my_tiles * nst;
+  Src src_cur, src_nxt;
+  // wait for stage g+1: its loads were issued at stage g-STAGES+2; issued
+  // after them are the loads of the next STAGES-3 stages (if the sequence
+  // has not ended) and at least ST stores.  Counting fewer operations than
+  // were issued only makes the wait stricter.
+  auto wait_next = [&](int g, auto STORES) __attribute__((always_inline)) {
+    constexpr int ST = decltype(STORES)::value;
+    if (g + STAGES - 2 < gtotal) wait_vmcnt<(STAGES - 3) * LPS + ST>();
+    else wait_vmcnt<ST>();
+  };
+  auto stage_body = [&](v16i (&X)[FM][FN], int g, int s, bool first, auto STORES_BEFORE,
+                        auto drain_fn) __attribute__((always_inline)) {
+    const int buf = g % STAGES;
+    load_frags(buf, 1, fa1, fb1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const v16i c = first ? v16i{} : X[i][j];
+        X[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa0[i], fb0[j], c, 0, 0, 0);
+      }
+#pragma unroll
+    for (int t = 0; t < FM + FN; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < gtotal) {
+      wait_next(g, STORES_BEFORE);
+      barrier_nofence();
+      const int gi = g + STAGES - 1;
+      if (gi < gtotal) {
+        const int si = s + STAGES - 1;
+        if (si < nst) issue(gi % STAGES, src_cur, si);
+        else issue(gi % STAGES, src_nxt, si - nst);
+      }
+      load_frags((g + 1) % STAGES, 0, fa0, fb0);
+    }
+    // stores of the drain must stay behind this stage's loads (wait counts)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        X[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa1[i], fb1[j], X[i][j], 0, 0, 0);
+    drain_fn();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto no_drain = []() __attribute__((always_inline)) {};
+
+  // One tile: X accumulates tile r; Y (if DRAIN) holds tile r-1, drained
+  // during stages 0..NB-1 (each stage drains one block: 16 stores).
+  auto run_tile = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int r, const Out& oy, auto DRAIN)
+      __attribute__((always_inline)) {
+    constexpr bool D = decltype(DRAIN)::value;
+    const int g0 = r * nst;
+    // stages that drain one block each (compile-time position b)
+    auto drain_stage = [&](auto BI) __attribute__((always_inline)) {
+      constexpr int b = decltype(BI)::value;
+      // stores issued after the loads this stage waits for: those of stages
+      // s-2 and s-1 of this tile (none before stage 0)
+      constexpr int ST = D ? (b >= 2 ? 32 : (b == 1 ? 16 : 0)) : 0;
+      if (b < nst) {
+        if (D) stage_body(X, g0 + b, b, b == 0, std::integral_constant<int, ST>(),
+                          [&]() __attribute__((always_inline)) { drain_block(Y, oy, BI); });
+        else stage_body(X, g0 + b, b, b == 0, std::integral_constant<int, 0>(), no_drain);
+      } else if (D) {
+        drain_block(Y, oy, BI);   // fewer stages than blocks: drain without MFMAs
+      }
+    };
+    static_for<0, NB>(drain_stage);
+    if (D) close_tile_hash(oy);
+    int s = NB;
+    if (s < nst) {   // first two stages after the drain still see its stores
+      stage_body(X, g0 + s, s, false, std::integral_constant<int, D ? 32 : 0>(), no_drain);
+      ++s;
+    }
+    if (s < nst) {
+      stage_body(X, g0 + s, s, false, std::integral_constant<int, D ? 16 : 0>(), no_drain);
+      ++s;
+    }
+    for (; s < nst; ++s) stage_body(X, g0 + s, s, false, std::integral_constant<int, 0>(), no_drain);
+  };
+
+  // acc0 accumulates the tile being multiplied; acc1 holds the previous
+  // tile while it is drained.  At a tile boundary acc0 is copied to acc1
+  // (AGPR to AGPR) and the next tile's first MFMAs restart acc0 from zero.
+  Out out_cur, out_prev;
+  if (my_tiles > 0) {
+    int tm, tn;
+    tile_coords(0, tm, tn);
+    make_src(0, tm, tn, src_cur);
+    make_out(0, tm, tn, out_cur);
+    if (my_tiles > 1) {
+      int tm1, tn1;
+      tile_coords(1, tm1, tn1);
+      make_src(1, tm1, tn1, src_nxt);
+    }
+    // prologue: the first STAGES-1 stages of the sequence
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) {
+      if (st < gtotal) {
+        if (st < nst) issue(st, src_cur, st);
+        else issue(st, src_nxt, st - nst);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();   // also publishes the row keys of tile 0
+    load_frags(0, 0, fa0, fb0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) tcol[j] = 0;
+
+    run_tile(acc0, acc1, 0, out_prev, std::false_type());
+    for (int r = 1; r < my_tiles; ++r) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc1[i][j] = acc0[i][j];
+      out_prev = out_cur;
+      // tile r starts: its sources become current; prepare tile r+1's
+      src_cur = src_nxt;
+      int a, b;
+      tile_coords(r, a, b);
+      make_out(r, a, b, out_cur);
+      if (r + 1 < my_tiles) {
+        int c, d;
+        tile_coords(r + 1, c, d);
+        make_src(r + 1, c, d, src_nxt);
+      }
+      run_tile(acc0, acc1, r, out_prev, std::true_type());
+    }
+    // the last tile
+    static_for<0, NB>([&](auto BI) __attribute__((always_inline)) { drain_block(acc0, out_cur, BI); });
+    close_tile_hash(out_cur);
+  }
+  if (p.do_hash) {
+    const uint64_t part = block_sum_u64<NT>(lane_hash, s_red);
+    hash_share_and_finalize<NT>(part, p.hash_parts, p.ticket, p.n_shares, blockIdx.x, (uint64_t)M,
+                                (uint64_t)N, p.hash_out, s_red, reinterpret_cast<int*>(s_red + NWAVES));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // split-K combine: acc = sum over splits (exact), then the same epilogue and
 // hash shares as the GEMM kernel; each thread owns 4 consecutive columns of a
@@ -500,17 +944,44 @@ splitk_combine_kernel(const GemmParams p) {
 // and the int8 MAC rate one workgroup sustains in the steady-state loop
 // (measured on MI355X with operands streaming through L2: LM-head weight
 // gradient 768x50304x8192, down-projection 8192x768x3072).
+// Tile configurations and the cost model that picks one.  Estimated time of
+// a non-persistent plan: rounds of resident workgroups x (MAC time of a tile
+// at `wg_macs` + its output tile at `wg_out_bw`); of a persistent plan:
+// tiles per workgroup x (MAC time + `tile_overhead`).  The rates were fitted
+// to timings on MI355X of the GPT-2-small shapes (8192x3072x768,
+// 8192x768x3072, 8192x50304x768, 768x50304x8192): at K = 768 the epilogue
+// and output write cost as much as the MACs.
 struct TileCfg {
-  int bm, bn, stages, per_cu;
-  double wg_macs;   // MAC/s of one resident workgroup
+  int bm, bn, per_cu;
+  double wg_macs;        // MAC/s of one resident workgroup in its main loop
+  double wg_out_bw;      // bytes/s of output one workgroup writes in its epilogue
+  double tile_overhead;  // persistent: seconds per tile beyond its MACs
+  bool persistent;       // one workgroup per CU walking tiles, epilogue drained under the next tile
 };
 static const TileCfg kCfgs[] = {
-    {256, 256, 4, 1, 4.5e12},   // eight waves (two per SIMD), 128x64 each
-    {256, 128, 4, 1, 3.0e12},   // four waves, 128x64 each
-    {128, 128, 4, 2, 1.25e12},  // four waves, 64x64 each
-    {256, 256, 4, 1, 4.0e12},   // four waves, 128x128 each (not chosen by default)
+    {256, 256, 1, 4.5e12, 20e9, 0, false},    // eight waves (two per SIMD), 128x64 each
+    {256, 128, 1, 3.3e12, 9.8e9, 0, false},   // four waves, 128x64 each
+    {128, 128, 2, 1.43e12, 6.9e9, 0, false},  // four waves, 64x64 each
+    {256, 256, 1, 4.0e12, 20e9, 0, false},    // four waves, 128x128 each (tests only)
+    {256, 128, 1, 3.0e12, 0, 6.0e-6, true},   // persistent, 128x64 per wave (tests only)
+    {128, 192, 1, 3.0e12, 0, 5.2e-6, true},   // persistent, four waves, 64x96 each
 };
-constexpr int kNumCfgs = 4;
+constexpr int kNumCfgs = 6;
+constexpr int kPersistStages = 4;
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 // Optional overrides for tests (the output never depends on the plan):
 // I8G_FORCE_TILE = index into kCfgs; I8G_FORCE_SPLITS = number of K splits
@@ -520,26 +991,48 @@ static int env_int(const char* name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
   GemmPlan best{};
   if (M <= 0 || N <= 0) return best;
   const int force_tile = env_int("I8G_FORCE_TILE", -1);
   const int force_splits = env_int("I8G_FORCE_SPLITS", 0);
-  // Estimated seconds: rounds of resident workgroups x (MAC time of one
-  // workgroup's share + the time to write its output tile at ~20 GB/s per
-  // CU; with two workgroups per CU one's stores overlap the other's MFMAs),
-  // plus the split-K partial round trip.
-  const double cu_out_bw = 20e9;
+  const int cus = device_cus();
+  // Estimated seconds (see TileCfg), plus the split-K partial round trip;
+  // no plan beats the whole output written at ~5 TB/s.
   const double mem_bw = 4.0e12;
+  const double write_bw = 5.0e12;
   double best_cost = 1e300;
+  const int64_t kstages = (K + BK - 1) / BK;
   for (int c = 0; c < kNumCfgs; ++c) {
     if (force_tile >= 0 && c != force_tile) continue;
-    if (force_tile < 0 && c == 3) continue;        // dominated by config 0; tests only
+    if (force_tile < 0 && (c == 3 || c == 4)) continue;   // tests only
     const TileCfg& t = kCfgs[c];
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = tm * tn;
+    if (t.persistent) {
+      if (!allow_persistent || K % BK != 0 || kstages < kPersistStages - 1 || tiles > INT32_MAX / 2)
+        continue;
+      if (force_splits > 1) continue;
+      const int64_t grid = tiles < cus ? tiles : cus;
+      const double rounds = std::ceil((double)tiles / (double)grid);
+      double cost = rounds * ((double)t.bm * t.bn * K / t.wg_macs + t.tile_overhead);
+      const double wr = (double)M * N * 4 / write_bw;
+      if (wr > cost) cost = wr;
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        best.cfg = c;
+        best.bm = t.bm;
+        best.bn = t.bn;
+        best.tiles_m = (int)tm;
+        best.tiles_n = (int)tn;
+        best.splits = 1;
+        best.k_per_split = (int)(kstages * BK);
+        best.grid = (int)grid;
+        best.persistent = true;
+      }
+      continue;
+    }
     const double slots = 256.0 * t.per_cu;
-    const int64_t kstages = (K + BK - 1) / BK;
     for (int s = 1; s <= 16; ++s) {
       if (force_splits > 0) {
         if (s != (force_splits < kstages ? force_splits : (int)kstages)) continue;
@@ -550,7 +1043,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
       const int s_eff = (int)((kstages + kps_st - 1) / kps_st);   // no empty split
       const double rounds = std::ceil((double)(tiles * s_eff) / slots);
       const double tile_s = (double)t.bm * t.bn * kps_st * BK / t.wg_macs +
-                            (double)t.bm * t.bn * 4 / cu_out_bw;
+                            (double)t.bm * t.bn * 4 / t.wg_out_bw;
       double cost = rounds * tile_s;
       if (s_eff > 1) cost += (double)s_eff * M * N * 8 / mem_bw + 5e-6;
       if (cost < best_cost * 0.999) {
@@ -562,21 +1055,24 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         best.tiles_n = (int)tn;
         best.splits = s_eff;
         best.k_per_split = (int)(kps_st * BK);
+        best.grid = (int)(tiles * s_eff);
+        best.persistent = false;
       }
     }
   }
-  if (best.bm == 0) {   // unreachable: every configuration has a one-split plan
+  if (best.bm == 0) {   // only when a forced configuration cannot run this shape
     best.cfg = 2; best.bm = best.bn = 128;
     best.tiles_m = (int)((M + 127) / 128); best.tiles_n = (int)((N + 127) / 128);
     best.splits = 1; best.k_per_split = (int)((K + BK - 1) / BK * BK);
+    best.grid = best.tiles_m * best.tiles_n;
+    best.persistent = false;
   }
-  const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
   if (best.splits > 1) {
     best.comb_x = (int)((N + 1023) / 1024);
     best.comb_y = (int)((M + COMB_ROWS - 1) / COMB_ROWS);
     best.hash_parts = best.comb_x * best.comb_y;
   } else {
-    best.hash_parts = (int)tiles;
+    best.hash_parts = best.grid;    // one share per workgroup
   }
   size_t bytes = kWsHeader + ((size_t)best.hash_parts * 8 + 255) / 256 * 256;
   best.partials_offset = bytes;
@@ -586,7 +1082,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream) {
-  const unsigned int grid = (unsigned int)((int64_t)plan.tiles_m * plan.tiles_n * plan.splits);
+  const unsigned int grid = (unsigned int)plan.grid;
   switch (plan.cfg) {
     case 0:
       hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 4, 4>), dim3(grid), dim3(512), 0, stream, p);
@@ -597,8 +1093,20 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
     case 2:
       hipLaunchKernelGGL((gemm_i8_dma_kernel<128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
       break;
-    default:
+    case 3:
       hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+    case 4:
+      if (p.relu)
+        hipLaunchKernelGGL((gemm_i8_persist_kernel<256, 128, 2, 2, 4, true>), dim3(grid), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_i8_persist_kernel<256, 128, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+    default:
+      if (p.relu)
+        hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, true>), dim3(grid), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
       break;
   }
   if (plan.splits > 1)

@@ -35,9 +35,15 @@ struct GemmPlan {
   int hash_parts;           // number of shares of S written before the finalize
   size_t partials_offset;   // hash shares at offset 0, split partials here
   size_t workspace_bytes;
+  int grid;                 // workgroups of the GEMM kernel
+  bool persistent;          // gemm_i8_persist_kernel (one workgroup per CU)
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+// Largest ldc (floats) the persistent kernel addresses with 32-bit buffer
+// offsets; larger leading dimensions are planned without it.
+constexpr int64_t kPersistMaxLdc = int64_t(1) << 23;
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent);
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
 
 hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,

@@ -187,6 +187,31 @@ def test_tile_and_split_invariance(g, tile):
         os.environ.pop("I8G_FORCE_SPLITS", None)
 
 
+# (M, N, K, relu): ragged edges; more tiles than CUs so that workgroups walk
+# several tiles (and some one fewer); K with fewer 64-byte stages than a
+# wave has output blocks, and with more
+PERSIST_CASES = [(300, 520, 3008, True), (4100, 2500, 192, False), (4100, 2500, 640, True),
+                 (1000, 1000, 1024, False), (2056, 6000, 256, True)]
+
+
+@pytest.mark.parametrize("tile", [4, 5])
+def test_persistent_kernel(g, tile):
+    """The persistent kernel (epilogue of one tile drained under the next
+    tile's MFMAs) against the oracle, every byte and the hash."""
+    rng = np.random.default_rng(90 + tile)
+    try:
+        os.environ["I8G_FORCE_TILE"] = str(tile)
+        for (m, n, k, relu) in PERSIST_CASES:
+            A = rng.standard_t(3, (m, k)).astype(F32)
+            B = rng.standard_normal((k, n)).astype(F32)
+            A[rng.random(m) < 0.02] = 0
+            say("persistent tile", tile, "MNK", m, n, k, "relu", relu)
+            got = run_method(g, A, B, relu=relu)
+            check_against_oracle(got, A, B, relu)
+    finally:
+        os.environ.pop("I8G_FORCE_TILE", None)
+
+
 def test_w2_mlp_full_size(g):
     """MLP up-projection (ReLU) and the down-projection on its output, full
     size, every output byte."""
