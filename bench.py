@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the bit-exact block-scaled int8 GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload mlp|head|w1|step]
+    python bench.py [--steps K] [--warmup W] [--workload mlp|head|step|w1]
 
 One step is one pass of the whole path over one batch: per GEMM,
 quantize_rows of the left operand, quantize_cols of the right one, and the
@@ -43,33 +43,52 @@ def log(*a):
 # the oracle step walk the same list
 # ---------------------------------------------------------------------------
 def make_workload(name):
+    """Returns (description, host tensors, GEMMs); a GEMM is (name, A source,
+    A mode, B source, B mode, relu, output name or None).  Mode 'rows' = the
+    source is quantized per row (it is A, or B transposed), 'cols' = per
+    column (it is B, or A transposed)."""
     from synth import inputs as S
     if name == "mlp":
         X, Wu, Wd = S.w2_inputs()
         desc = ("GPT-2-small MLP: up 8192x768 @ 768x3072 (ReLU), then down "
                 "8192x3072 @ 3072x768 on the up output; quantize passes included")
-        gemms = [("up", "X", "Wu", True, "H"), ("down", "H", "Wd", False, None)]
+        gemms = [("up", "X", "rows", "Wu", "cols", True, "H"),
+                 ("down", "H", "rows", "Wd", "cols", False, None)]
         return desc, {"X": X, "Wu": Wu, "Wd": Wd}, gemms
     if name == "head":
         X, Wh = S.w3_fwd_inputs()
         _, dY = S.w3_wgrad_inputs()
         desc = ("GPT-2-small LM head: forward 8192x768 @ 768x50304 and weight "
                 "gradient X^T (768x8192) @ dY (8192x50304); quantize passes included")
-        gemms = [("head_fwd", "X", "Wh", False, None), ("head_wgrad", "X^T", "dY", False, None)]
+        gemms = [("head_fwd", "X", "rows", "Wh", "cols", False, None),
+                 ("head_wgrad", "X", "cols", "dY", "cols", False, None)]
         return desc, {"X": X, "Wh": Wh, "dY": dY}, gemms
+    if name == "step":
+        tensors, gemms = {}, []
+        for gm in S.step_gemms():
+            a, am, b, bm = gm.operands
+            for src in (a, b):
+                key = f"{gm.linear}.{src}"
+                if key not in tensors:
+                    tensors[key] = S.step_tensor(gm.linear, src, gm.d_in, gm.d_out)
+            gemms.append((f"{gm.linear}.{gm.kind}", f"{gm.linear}.{a}", am, f"{gm.linear}.{b}", bm,
+                          False, None))
+        desc = ("GPT-2-small training step: the 147 GEMMs of 12 layers x (QKV, attention "
+                "out, MLP up, MLP down) forward, dgrad and wgrad plus the LM head "
+                "(8192 token rows); quantize passes included")
+        return desc, tensors, gemms
     if name == "w1":
         A, B = S.w1_inputs()
-        return "single 256x256x256 GEMM", {"A": A, "B": B}, [("w1", "A", "B", False, None)]
+        return ("single 256x256x256 GEMM", {"A": A, "B": B},
+                [("w1", "A", "rows", "B", "cols", False, None)])
     raise SystemExit(f"unknown workload {name}")
 
 
-def gemm_mnk(tensors, a_src, b_src):
-    if a_src.endswith("^T"):
-        a = tensors[a_src[:-2]]
-        M, K = a.shape[1], a.shape[0]
-    else:
-        M, K = tensors[a_src].shape
-    N = tensors[b_src].shape[1]
+def gemm_mnk(shapes, a_src, a_mode, b_src, b_mode):
+    """(M, N, K) of a GEMM from its operands' shapes and modes."""
+    M, K = shapes[a_src] if a_mode == "rows" else shapes[a_src][::-1]
+    K2, N = shapes[b_src] if b_mode == "cols" else shapes[b_src][::-1]
+    assert K == K2, (a_src, b_src)
     return M, N, K
 
 
@@ -87,18 +106,12 @@ class GpuStep:
         self.gemms = []
         ws_bytes = 256
         shapes = {k: tuple(v.shape) for k, v in tensors.items()}
-        for (name, a_src, b_src, relu, out_name) in gemms:
-            if a_src.endswith("^T"):
-                K, M = shapes[a_src[:-2]]
-                a_mode, a_key = "cols", a_src[:-2]
-            else:
-                M, K = shapes[a_src]
-                a_mode, a_key = "rows", a_src
-            N = shapes[b_src][1]
+        for (name, a_src, a_mode, b_src, b_mode, relu, out_name) in gemms:
+            M, N, K = gemm_mnk(shapes, a_src, a_mode, b_src, b_mode)
             shapes[out_name or name] = (M, N)
             ld = (K + 15) // 16 * 16
-            e = dict(name=name, M=M, N=N, K=K, relu=relu, a_mode=a_mode, a_key=a_key, b_key=b_src,
-                     out=out_name or name,
+            e = dict(name=name, M=M, N=N, K=K, relu=relu, a_mode=a_mode, a_key=a_src,
+                     b_mode=b_mode, b_key=b_src, out=out_name or name,
                      QA=torch.empty((M, ld), dtype=torch.int8, device=dev),
                      sA=torch.empty(M, dtype=torch.float32, device=dev),
                      QB=torch.empty((N, ld), dtype=torch.int8, device=dev),
@@ -128,7 +141,7 @@ class GpuStep:
             self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])
             if record is not None:
                 marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
-            self._q("cols", self.t[e["b_key"]], e["QB"], e["sB"], e["ld"])
+            self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ld"])
             if record is not None:
                 marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
             flags = (1 if e["relu"] else 0) | 2
@@ -150,36 +163,51 @@ class GpuStep:
 # ---------------------------------------------------------------------------
 # CPU oracle step (the cpu_baseline leg)
 # ---------------------------------------------------------------------------
-def oracle_step(tensors, gemms):
-    import numpy as np
+def oracle_step(tensors, gemms, budget_s=None):
+    """The CPU oracle over the GEMMs in order; with a time budget it stops
+    after the GEMM that crosses it.  Returns (hashes, int8 ops done)."""
     from oracle import hashref, ref
     t = dict(tensors)
-    hashes = []
-    for (name, a_src, b_src, relu, out_name) in gemms:
-        if a_src.endswith("^T"):
-            QA, sA = ref.quantize_cols(t[a_src[:-2]])
-        else:
-            QA, sA = ref.quantize_rows(t[a_src])
-        QB, sB = ref.quantize_cols(t[b_src])
+    shapes = {k: tuple(v.shape) for k, v in t.items()}
+    hashes, ops = [], 0.0
+    t0 = time.perf_counter()
+    for (name, a_src, a_mode, b_src, b_mode, relu, out_name) in gemms:
+        M, N, K = gemm_mnk(shapes, a_src, a_mode, b_src, b_mode)
+        q = {"rows": ref.quantize_rows, "cols": ref.quantize_cols}
+        QA, sA = q[a_mode](t[a_src])
+        QB, sB = q["cols" if b_mode == "cols" else "rows"](t[b_src])
         C = ref.gemm_i8_blockscaled(QA, sA, QB, sB, relu)
         t[out_name or name] = C
+        shapes[out_name or name] = C.shape
         hashes.append(hashref.output_hash(C))
+        ops += 2.0 * M * N * K
         del QA, QB
-    return hashes
+        if budget_s is not None and time.perf_counter() - t0 >= budget_s:
+            break
+    return hashes, ops
 
 
 def cpu_baseline(tensors, gemms, ops, budget_s=10.0):
+    """The oracle timed on this host: whole steps (one to three, about
+    budget_s of work) when a step is short, else the leading GEMMs of one
+    step up to the budget.  Returns (record, oracle hashes of the GEMMs it ran)."""
     from threadpoolctl import threadpool_info
     blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
     threads = max([d.get("num_threads", 1) for d in blas] or [1])
-    times, hashes = [], None
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        hashes = oracle_step(tensors, gemms)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= budget_s or len(times) >= 3:
-            break
+    t0 = time.perf_counter()
+    hashes, done = oracle_step(tensors, gemms, budget_s)
+    first = time.perf_counter() - t0
+    if len(hashes) < len(gemms):
+        return {"value": done / first / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+                "sample": f"the first {len(hashes)} of the step's {len(gemms)} GEMMs "
+                          f"({done / 1e9:.1f} GOP) in {first:.1f} s; numpy float32 per-op "
+                          f"quantize/epilogue (1 thread), float64 BLAS contraction "
+                          f"({threads} threads), numpy uint64 hash"}, hashes
+    times = [first]
+    while time.perf_counter() - t0 < budget_s and len(times) < 3:
+        t1 = time.perf_counter()
+        oracle_step(tensors, gemms)
+        times.append(time.perf_counter() - t1)
     sec = statistics.median(times)
     return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} full step(s) of the same workload, median {sec:.2f} s; "
@@ -216,7 +244,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "w1"])
+    ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "step", "w1"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="also run one plain device copy of MB MiB (a reference for HBM "
@@ -283,11 +311,12 @@ def main():
             bound = "mfma" if gops / nbytes >= RIDGE else "hbm"
             shape = f"{M}x{N}x{K}"
         else:
-            rows, cols = (M, K) if label == "quantize_A" else (K, N)
-            if label == "quantize_A" and e["a_mode"] == "cols":
-                rows, cols = K, M
-            gops, nbytes, bound = 0.0, 5 * rows * cols + 4 * (cols if label == "quantize_B" or e["a_mode"] == "cols" else rows), "hbm"
-            shape = f"{rows}x{cols} ({'cols' if label == 'quantize_B' or e['a_mode'] == 'cols' else 'rows'})"
+            # the quantized source tensor and the direction of its scales
+            mode = e["a_mode"] if label == "quantize_A" else e["b_mode"]
+            rows, cols = step.t[e["a_key"] if label == "quantize_A" else e["b_key"]].shape
+            nscale = rows if mode == "rows" else cols
+            gops, nbytes, bound = 0.0, 5 * rows * cols + 4 * nscale, "hbm"
+            shape = f"{rows}x{cols} ({mode})"
         if bound == "mfma":
             ach, peak, unit = gops / (avg * 1e-6) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
         else:
@@ -308,7 +337,7 @@ def main():
     if not a.no_cpu_baseline:
         log("[bench] cpu_baseline: oracle on the host")
         cpu, cpu_hashes = cpu_baseline(tensors, gemms, ops)
-        parity = cpu_hashes == gpu_hashes
+        parity = cpu_hashes == gpu_hashes[:len(cpu_hashes)]
         log(f"[bench] oracle {cpu['value']:.4f} TOPS, parity {parity}")
 
     out = {

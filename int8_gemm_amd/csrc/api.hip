@@ -122,6 +122,7 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
   p.hash_parts = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
   p.n_shares = plan.hash_parts;
   p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
+  p.comb_rows = plan.comb_rows;
   p.hash_out = hash;
   return hip_status(launch_gemm(p, plan, as_stream(stream)));
 }

@@ -872,9 +872,10 @@ gemm_i8_persist_kernel(const GemmParams p) {
 // ---------------------------------------------------------------------------
 // split-K combine: acc = sum over splits (exact), then the same epilogue and
 // hash shares as the GEMM kernel; each thread owns 4 consecutive columns of a
-// band of COMB_ROWS rows.
+// band of p.comb_rows rows (chosen so that the grid has about a thousand
+// workgroups: the sums are memory-bound and need the whole chip).
 // ---------------------------------------------------------------------------
-constexpr int COMB_ROWS = 32;
+constexpr int COMB_ROWS_MAX = 32;
 
 __global__ void __launch_bounds__(256)
 splitk_combine_kernel(const GemmParams p) {
@@ -883,8 +884,8 @@ splitk_combine_kernel(const GemmParams p) {
   const int M = p.M, N = p.N;
   const int tid = threadIdx.x;
   const int c0 = (blockIdx.x * 256 + tid) * 4;
-  const int r0 = blockIdx.y * COMB_ROWS;
-  const int r1 = r0 + COMB_ROWS < M ? r0 + COMB_ROWS : M;
+  const int r0 = blockIdx.y * p.comb_rows;
+  const int r1 = r0 + p.comb_rows < M ? r0 + p.comb_rows : M;
   const bool relu = p.relu != 0;
   const int64_t plane = (int64_t)M * N;
   uint64_t t[4] = {0, 0, 0, 0};
@@ -1069,7 +1070,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
   }
   if (best.splits > 1) {
     best.comb_x = (int)((N + 1023) / 1024);
-    best.comb_y = (int)((M + COMB_ROWS - 1) / COMB_ROWS);
+    int64_t rows_per = (M * best.comb_x + 1023) / 1024;   // about 1024 workgroups
+    rows_per = rows_per < 1 ? 1 : (rows_per > COMB_ROWS_MAX ? COMB_ROWS_MAX : rows_per);
+    best.comb_rows = (int)rows_per;
+    best.comb_y = (int)((M + rows_per - 1) / rows_per);
     best.hash_parts = best.comb_x * best.comb_y;
   } else {
     best.hash_parts = best.grid;    // one share per workgroup

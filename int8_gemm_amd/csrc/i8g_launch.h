@@ -22,6 +22,7 @@ struct GemmParams {
   unsigned int* ticket;             // workspace word counting finished shares (zero between calls)
   int n_shares;                     // shares of S written by the kernel that ends the call
   int* partials;                    // split-K int32 partial sums, [split][M][N]
+  int comb_rows;                    // rows per split-K combine workgroup
   uint64_t* hash_out;
 };
 
@@ -32,6 +33,7 @@ struct GemmPlan {
   int splits;
   int k_per_split;          // bytes of K per split (multiple of 64)
   int comb_x, comb_y;       // split-K combine grid
+  int comb_rows;            // rows per combine workgroup
   int hash_parts;           // number of shares of S written before the finalize
   size_t partials_offset;   // hash shares at offset 0, split partials here
   size_t workspace_bytes;

@@ -12,15 +12,13 @@
 //    1024-thread workgroup per row beyond that (registers up to 65536
 //    elements, a second read from cache above).  The row max is a wave
 //    butterfly reduction (plus LDS across waves).
-//  * cols, up to 8192 rows: one kernel, a workgroup per column band holding
-//    the band in registers (see qcols_reg_kernel).
-//  * cols, taller: the column max needs every row first, so it is a
-//    grid-wide reduction: zero the scale array, a column-max kernel combines
-//    workgroup maxima with atomicMax on the bit patterns of |x| (for
-//    non-negative floats the integer order is the float order, so the
-//    result is exact and order-free), then a quantize kernel transposes
-//    64x64 tiles through LDS into the K-contiguous int8 output, and a last
-//    kernel turns the stored maxima into scales.
+//  * cols, short columns: one kernel, a workgroup per column band holding
+//    the band in registers (see qcols_reg_kernel);
+//  * cols, tall columns (bands of at most 8 columns would not read whole
+//    cache lines): two passes over X, a column-scale pass and a
+//    quantize-transpose pass (see qcols_scale_kernel).
+#include <cstdlib>
+
 #include "i8g_device.h"
 #include "i8g_launch.h"
 
@@ -179,35 +177,55 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
 }
 
 // ---------------------------------------------------------------------------
-// cols
+// cols, two passes (tall columns): the column scale needs every row first.
+//  1. qcols_init_kernel writes the scale floor RN(1e-8) to every scale;
+//  2. qcols_scale_kernel reads X in full, coalesced rows, keeps a per-thread
+//     max of |x| per column over its rows, turns it into a partial scale
+//     max(RN(a/127), RN(1e-8)) and combines partial scales with atomicMax on
+//     their bit patterns.  RN and the floor are monotone, so the largest
+//     partial scale is the scale of the column max, exactly and in any order,
+//     and positive floats order like their bit patterns;
+//  3. qcols_quant_kernel reads X again (it is usually still in the last-level
+//     cache), quantizes 64x64 tiles with inv = RN(1/s), transposes them
+//     through LDS and writes K-contiguous rows of Qt.
 // ---------------------------------------------------------------------------
-__global__ void fill_zero_u32_kernel(unsigned int* p, int64_t n) {
+__global__ void qcols_init_kernel(float* scale, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  if (i < n) scale[i] = scale_floor();
 }
 
-// Column maxima of a ROWS_PER_WG x 256 block; combined across workgroups
-// with atomicMax on the bit patterns of |x| (stored in `maxbits`).
-constexpr int QC_ROWS = 64;
+constexpr int QS_ROWS = 64;     // rows per workgroup of qcols_scale_kernel
+constexpr int QS_COLS = 256;    // columns per workgroup (64 lanes x 4)
 
 __global__ void __launch_bounds__(256)
-qcols_max_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
-                 unsigned int* __restrict__ maxbits, int vec_in) {
-  __shared__ float red[4][256];
+qcols_scale_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                   float* __restrict__ scale, int vec_in) {
+  __shared__ float red[4][QS_COLS];
   const int tid = threadIdx.x;
   const int cg = tid & 63, ph = tid >> 6;          // column group of 4, row phase
-  const int64_t c = (int64_t)blockIdx.x * 256 + cg * 4;
-  const int64_t r0 = (int64_t)blockIdx.y * QC_ROWS;
-  int64_t r1 = r0 + QC_ROWS;
-  if (r1 > rows) r1 = rows;
+  const int64_t c = (int64_t)blockIdx.x * QS_COLS + cg * 4;
+  const int64_t r0 = (int64_t)blockIdx.y * QS_ROWS;
   float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < cols) {
-    for (int64_t r = r0 + ph; r < r1; r += 4) {
-      float4 v = load4(X + r * ldx, c, cols, vec_in);
-      m.x = fmaxf(m.x, fabsf(v.x));
-      m.y = fmaxf(m.y, fabsf(v.y));
-      m.z = fmaxf(m.z, fabsf(v.z));
-      m.w = fmaxf(m.w, fabsf(v.w));
+    if (r0 + QS_ROWS <= rows) {
+      float4 v[QS_ROWS / 4];
+#pragma unroll
+      for (int i = 0; i < QS_ROWS / 4; ++i) v[i] = load4(X + (r0 + ph + 4 * i) * ldx, c, cols, vec_in);
+#pragma unroll
+      for (int i = 0; i < QS_ROWS / 4; ++i) {
+        m.x = fmaxf(m.x, fabsf(v[i].x));
+        m.y = fmaxf(m.y, fabsf(v[i].y));
+        m.z = fmaxf(m.z, fabsf(v[i].z));
+        m.w = fmaxf(m.w, fabsf(v[i].w));
+      }
+    } else {
+      for (int64_t r = r0 + ph; r < rows; r += 4) {
+        const float4 v = load4(X + r * ldx, c, cols, vec_in);
+        m.x = fmaxf(m.x, fabsf(v.x));
+        m.y = fmaxf(m.y, fabsf(v.y));
+        m.z = fmaxf(m.z, fabsf(v.z));
+        m.w = fmaxf(m.w, fabsf(v.w));
+      }
     }
   }
   red[ph][cg * 4 + 0] = m.x;
@@ -215,16 +233,17 @@ qcols_max_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_
   red[ph][cg * 4 + 2] = m.z;
   red[ph][cg * 4 + 3] = m.w;
   __syncthreads();
-  const float t = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-  const int64_t col = (int64_t)blockIdx.x * 256 + tid;
-  if (col < cols) atomicMax(maxbits + col, __float_as_uint(t));
+  const float a = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+  const int64_t col = (int64_t)blockIdx.x * QS_COLS + tid;
+  if (col < cols)
+    atomicMax(reinterpret_cast<unsigned int*>(scale) + col, __float_as_uint(scale_of_absmax(a)));
 }
 
 // Quantize a 64 (rows of X = k) x 64 (columns of X = j) tile with the column
 // scales, transpose through LDS, write 64 rows of Qt (64 bytes each).
 __global__ void __launch_bounds__(256)
 qcols_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
-                   int8_t* __restrict__ Qt, int64_t ldqt, const unsigned int* __restrict__ maxbits,
+                   int8_t* __restrict__ Qt, int64_t ldqt, const float* __restrict__ scale,
                    int vec_in, int vec_out) {
   __shared__ float s_inv[64];
   __shared__ unsigned int tq[64][17];              // [j][k/4], padded
@@ -232,24 +251,26 @@ qcols_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
   const int64_t j0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
   if (tid < 64) {
     const int64_t j = j0 + tid;
-    const float a = j < cols ? __uint_as_float(maxbits[j]) : 0.0f;
-    s_inv[tid] = recip_rn(scale_of_absmax(a));
+    s_inv[tid] = j < cols ? recip_rn(scale[j]) : 0.0f;
   }
   __syncthreads();
   const int cg = tid & 15, rr = tid >> 4;          // 16 groups of 4 columns, 16 rows
   const float i0 = s_inv[cg * 4], i1 = s_inv[cg * 4 + 1], i2 = s_inv[cg * 4 + 2], i3 = s_inv[cg * 4 + 3];
   // each thread quantizes rows k = 4*rr .. 4*rr+3 of its 4 columns, so it can
   // pack 4 consecutive k of one column into one 32-bit word of tq.
-  unsigned int w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+  float4 v[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t k = k0 + rr * 4 + e;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < rows) v = load4(X + k * ldx, j0 + cg * 4, cols, vec_in);
-    w0 |= (unsigned int)(quantize1(v.x, i0) & 0xFF) << (8 * e);
-    w1 |= (unsigned int)(quantize1(v.y, i1) & 0xFF) << (8 * e);
-    w2 |= (unsigned int)(quantize1(v.z, i2) & 0xFF) << (8 * e);
-    w3 |= (unsigned int)(quantize1(v.w, i3) & 0xFF) << (8 * e);
+    v[e] = k < rows ? load4(X + k * ldx, j0 + cg * 4, cols, vec_in) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  unsigned int w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w0 |= (unsigned int)(quantize1(v[e].x, i0) & 0xFF) << (8 * e);
+    w1 |= (unsigned int)(quantize1(v[e].y, i1) & 0xFF) << (8 * e);
+    w2 |= (unsigned int)(quantize1(v[e].z, i2) & 0xFF) << (8 * e);
+    w3 |= (unsigned int)(quantize1(v[e].w, i3) & 0xFF) << (8 * e);
   }
   tq[cg * 4 + 0][rr] = w0;
   tq[cg * 4 + 1][rr] = w1;
@@ -271,11 +292,6 @@ qcols_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
     const unsigned int w[4] = {a, b, c, d};
     for (int e = 0; e < 16 && k + e < rows; ++e) dst[k + e] = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
   }
-}
-
-__global__ void qcols_scale_kernel(float* scale, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) scale[i] = scale_of_absmax(scale[i]);   // scale[i] holds the column max
 }
 
 // ---------------------------------------------------------------------------
@@ -395,7 +411,11 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
                                 int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Qt % 16 == 0) && (ldqt % 16 == 0);
-  const int bc = rows > 0 ? qcols_band(rows, cols) : 0;
+  int bc = rows > 0 ? qcols_band(rows, cols) : 0;
+  // I8G_QCOLS_TWO_PASS=1 forces the two-pass kernels (tests and timing; the
+  // bytes never depend on the path)
+  const char* force = getenv("I8G_QCOLS_TWO_PASS");
+  if (force && force[0] == '1') bc = 0;
   if (bc > 0) {
     const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
     switch (bc) {
@@ -407,19 +427,17 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
     }
     return hipGetLastError();
   }
-  unsigned int* maxbits = reinterpret_cast<unsigned int*>(scale);
-  hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
-                     stream, maxbits, cols);
-  if (rows > 0) {
-  hipLaunchKernelGGL(qcols_max_kernel,
-                     dim3((unsigned int)((cols + 255) / 256), (unsigned int)((rows + QC_ROWS - 1) / QC_ROWS)),
-                     dim3(256), 0, stream, X, rows, cols, ldx, maxbits, vec_in);
-  hipLaunchKernelGGL(qcols_quant_kernel,
-                     dim3((unsigned int)((cols + 63) / 64), (unsigned int)((rows + 63) / 64)), dim3(256), 0,
-                     stream, X, rows, cols, ldx, Qt, ldqt, (const unsigned int*)maxbits, vec_in, vec_out);
-  }
-  hipLaunchKernelGGL(qcols_scale_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(qcols_init_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
                      stream, scale, cols);
+  if (rows > 0) {
+    hipLaunchKernelGGL(qcols_scale_kernel,
+                       dim3((unsigned int)((cols + QS_COLS - 1) / QS_COLS),
+                            (unsigned int)((rows + QS_ROWS - 1) / QS_ROWS)),
+                       dim3(256), 0, stream, X, rows, cols, ldx, scale, vec_in);
+    hipLaunchKernelGGL(qcols_quant_kernel,
+                       dim3((unsigned int)((cols + 63) / 64), (unsigned int)((rows + 63) / 64)),
+                       dim3(256), 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out);
+  }
   return hipGetLastError();
 }
 

@@ -134,6 +134,23 @@ def test_quantize_cols_parity(g, rows, cols):
     assert_bits(s.cpu().numpy(), so, "scale")
 
 
+@pytest.mark.parametrize("rows,cols", QC_SHAPES)
+def test_quantize_cols_two_pass(g, rows, cols):
+    """The two-pass column kernels (scale pass with atomicMax on partial
+    scales, then quantize-transpose) on every shape, forced."""
+    say("quantize_cols two-pass", rows, cols)
+    X = np.ascontiguousarray(_quant_input(cols, rows, rows * 7919 + cols + 1).T)
+    os.environ["I8G_QCOLS_TWO_PASS"] = "1"
+    try:
+        Qt, s = g.quantize_cols(to_dev(X))
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("I8G_QCOLS_TWO_PASS", None)
+    Qo, so = ref.quantize_cols(X)
+    assert_bits(Qt.cpu().numpy(), Qo, "Qt")
+    assert_bits(s.cpu().numpy(), so, "scale")
+
+
 def test_quantize_cols_unaligned(g):
     say("quantize_cols unaligned view")
     base = np.ascontiguousarray(_quant_input(130, 67, 6).T)      # 67 x 130
