@@ -3,19 +3,21 @@
 
     python bench.py [--steps K] [--warmup W] [--workload mlp|head|step|w1]
 
-One step is one pass of the whole path over one batch: per GEMM,
-quantize_rows of the left operand, quantize_cols of the right one, and the
-int8 GEMM with its fused epilogue and output hash.  The default workload is
-the GPT-2-small MLP (batch 8 x sequence 1024 = 8192 token rows): the
-up-projection 8192x768 @ 768x3072 with ReLU, then the down-projection
-8192x3072 @ 3072x768 on its output.  Inputs are seeded synthetic f32
-tensors, resident in HBM before timing starts.
+One step is one pass of the whole path over one batch: per GEMM, the
+quantize pass of each operand (per row, or per column with the transposed
+int8 output) and the int8 GEMM with its fused epilogue and output hash.  The
+default workload is the GPT-2-small MLP (batch 8 x sequence 1024 = 8192
+token rows): the up-projection 8192x768 @ 768x3072 with ReLU, then the
+down-projection 8192x3072 @ 3072x768 on its output.  Inputs are seeded
+synthetic f32 tensors, resident in HBM before timing starts.
 
 Prints ONE JSON line: value = int8 GEMM operations (2MNK summed over the
-step's GEMMs) per second of the whole step, in TOPS; `roofline` for the
-step's dominant kernel from HIP events recorded around every launch of the
-timed steps; `cpu_baseline` = the CPU oracle timed on this host on a full
-step; `parity` = whether the oracle's output hashes equal the GPU's.
+step's GEMMs) per second of the whole step, in TOPS, from HIP events around
+K steps, each step one replay of the step captured in a HIP graph (--eager:
+launched call by call); `roofline` for the step's dominant kernel, whose
+device duration is timed with HIP events around a batch of back-to-back
+launches of that call; `cpu_baseline` = the CPU oracle timed on this host;
+`parity` = whether the oracle's output hashes equal the GPU's.
 """
 import argparse
 import hashlib
@@ -131,30 +133,30 @@ class GpuStep:
         if rc:
             raise RuntimeError(self.lib.i8g_status_string(rc).decode())
 
-    def run(self, record=None):
-        lib = self.lib
+    def _gemm(self, e):
+        flags = (1 if e["relu"] else 0) | 2
+        rc = self.lib.gemm_i8_blockscaled(e["QA"].data_ptr(), e["ld"], e["sA"].data_ptr(),
+                                          e["QB"].data_ptr(), e["ld"], e["sB"].data_ptr(),
+                                          e["M"], e["N"], e["K"], e["C"].data_ptr(), e["N"], flags,
+                                          e["h"].data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                                          self.sp)
+        if rc:
+            raise RuntimeError(self.lib.i8g_status_string(rc).decode())
+
+    def calls(self, e):
+        """The three calls of one GEMM of the step, as (label, function)."""
+        return (("quantize_A", lambda: self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])),
+                ("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ld"])),
+                ("gemm", lambda: self._gemm(e)))
+
+    def run(self):
+        """Enqueue one step on torch's current stream (a graph capture switches
+        it, so it is read at every call)."""
+        self.stream = self.torch.cuda.current_stream(self.dev)
+        self.sp = self.stream.cuda_stream
         for e in self.gemms:
-            marks = []
-            ev = self.torch.cuda.Event
-            if record is not None:
-                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
-            self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])
-            if record is not None:
-                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
-            self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ld"])
-            if record is not None:
-                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
-            flags = (1 if e["relu"] else 0) | 2
-            rc = lib.gemm_i8_blockscaled(e["QA"].data_ptr(), e["ld"], e["sA"].data_ptr(),
-                                         e["QB"].data_ptr(), e["ld"], e["sB"].data_ptr(),
-                                         e["M"], e["N"], e["K"], e["C"].data_ptr(), e["N"], flags,
-                                         e["h"].data_ptr(), self.ws.data_ptr(), self.ws.numel(),
-                                         self.sp)
-            if rc:
-                raise RuntimeError(lib.i8g_status_string(rc).decode())
-            if record is not None:
-                marks.append(ev(enable_timing=True)); marks[-1].record(self.stream)
-                record.append((e, marks))
+            for _, fn in self.calls(e):
+                fn()
 
     def hashes(self):
         return [self.g.hash_value(e["h"]) for e in self.gemms]
@@ -246,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "step", "w1"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of the step captured in a HIP graph")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="also run one plain device copy of MB MiB (a reference for HBM "
                          "byte counters collected by a profiler around this run)")
@@ -277,29 +281,74 @@ def main():
     torch.cuda.synchronize()
     gpu_hashes = step.hashes()
 
-    # timed region: exactly K steps, events around every call
-    record = []
-    log(f"[bench] timing {a.steps} steps")
+    # One step captured in a HIP graph (the library allocates nothing, launches
+    # only kernels on the given stream and leaves its workspace header zero, so
+    # a replay repeats the step exactly).  Every replay of the check below,
+    # with eager steps between them, must reproduce the eager hashes.
+    graph = None
+    if not a.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.run()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for e in step.gemms:
+                e["h"].zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if step.hashes() != gpu_hashes:
+                raise SystemExit("graph replay changed the output hashes")
+            step.run()
+            torch.cuda.synchronize()
+            if step.hashes() != gpu_hashes:
+                raise SystemExit("eager step after a replay changed the output hashes")
+        for _ in range(a.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly K steps (graph replays, or eager launches)
+    log(f"[bench] timing {a.steps} steps ({'eager' if graph is None else 'graph replay'})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    start.record(step.stream)
+    stream = torch.cuda.current_stream()
+    start.record(stream)
     for _ in range(a.steps):
-        step.run(record)
-    stop.record(step.stream)
+        if graph is None:
+            step.run()
+        else:
+            graph.replay()
+    stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(stop)
     ms_per_step = gpu_ms / a.steps
     value = ops / (ms_per_step * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.4f} ms/step (wall {wall / a.steps * 1e3:.4f} ms/step), {value:.1f} TOPS")
+    if step.hashes() != gpu_hashes:
+        raise SystemExit("timed steps changed the output hashes")
 
-    # per-call durations (us) from the events of the timed steps
+    # Per-call device durations: every call of the step launched R times back
+    # to back on the same stream, behind a short sleep kernel so that the host
+    # runs ahead of the GPU, with one event pair around the R launches.
     per = {}
-    for e, m in record:
-        for label, i in (("quantize_A", 0), ("quantize_B", 1), ("gemm", 2)):
-            per.setdefault((e["name"], label), []).append(m[i].elapsed_time(m[i + 1]) * 1e3)
+    reps = max(5, min(a.steps, 50))
+    for e in step.gemms:
+        for label, fn in step.calls(e):
+            torch.cuda.synchronize()
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(2_000_000)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(step.stream)
+            for _ in range(reps):
+                fn()
+            e1.record(step.stream)
+            torch.cuda.synchronize()
+            per[(e["name"], label)] = [e0.elapsed_time(e1) * 1e3 / reps]
+    if step.hashes() != gpu_hashes:
+        raise SystemExit("repeated calls changed the output hashes")
     kernels = []
     for (name, label), us in per.items():
         e = next(x for x in step.gemms if x["name"] == name)
@@ -363,6 +412,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "gpu_hashes": [f"{h:#018x}" for h in gpu_hashes],
+        "launch": "eager" if graph is None else "hip graph replay per step",
     }
     print(json.dumps(out), flush=True)
 
