@@ -253,9 +253,22 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   }
 }
 
+// LDS bytes of the ring (and, reused after the main loop, of the epilogue).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
-gemm_i8_dma_kernel(const GemmParams p) {
+constexpr int dma_smem_bytes() {
+  constexpr int NWAVES = WAVES_M * WAVES_N, WTN = BN / WAVES_N;
+  constexpr int STAGE = (BM + BN) * BK;
+  constexpr int EPI_BYTES = NWAVES * 32 * (WTN + 8) * 4 + 2 * BM * 4 + 128;
+  return STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
+}
+
+// The main loop of one tile over K bytes [k_begin, k_end): acc is set to
+// the exact int32 sums.  Called by every wave of the workgroup; the caller
+// makes sure no wave still reads the LDS ring of a previous call.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+__device__ __forceinline__ void dma_mainloop(
+    const GemmParams& p, int8_t* smem, int tm, int tn, int k_begin, int k_end,
+    v16i (&acc)[BM / WAVES_M / 32][BN / WAVES_N / 32]) {
   constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves");
   static_assert(STAGES >= 3, "the ring needs at least three stages");
@@ -265,19 +278,10 @@ gemm_i8_dma_kernel(const GemmParams p) {
   constexpr int A_INS = BM / (16 * NWAVES), B_INS = BN / (16 * NWAVES);   // 16-row blocks per wave
   static_assert(A_INS * 16 * NWAVES == BM && B_INS * 16 * NWAVES == BN, "rows per stage");
   constexpr int LPS = A_INS + B_INS;                   // load instructions per wave per stage
-  constexpr int EPI_BYTES = NWAVES * 32 * (WTN + 8) * 4 + 2 * BM * 4 + 128;
-  constexpr int SMEM = STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
-  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  int tm, tn, split;
-  map_workgroup(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.splits, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int M = p.M, N = p.N, K = p.K;
-  const int k_begin = split * p.k_per_split;
-  int k_end = k_begin + p.k_per_split;
-  if (k_end > K) k_end = K;
+  const int M = p.M, N = p.N;
   const int klen = k_end > k_begin ? k_end - k_begin : 0;
   const int nfull = klen / BK;
   const bool tail = (klen % BK) != 0;
@@ -307,7 +311,6 @@ gemm_i8_dma_kernel(const GemmParams p) {
     for (int q = 0; q < B_INS; ++q) dma_load16(gb[q] + kt * BK, base + A_BYTES + q * NWAVES * 1024);
   };
 
-  v16i acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -423,6 +426,20 @@ gemm_i8_dma_kernel(const GemmParams p) {
   }
   wait_vmcnt<0>();
   __syncthreads();
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
+gemm_i8_dma_kernel(const GemmParams p) {
+  constexpr int FM = BM / WAVES_M / 32, FN = BN / WAVES_N / 32;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[dma_smem_bytes<BM, BN, WAVES_M, WAVES_N, STAGES>()];
+  int tm, tn, split;
+  map_workgroup(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.splits, tm, tn, split);
+  const int k_begin = split * p.k_per_split;
+  int k_end = k_begin + p.k_per_split;
+  if (k_end > p.K) k_end = p.K;
+  v16i acc[FM][FN];
+  dma_mainloop<BM, BN, WAVES_M, WAVES_N, STAGES>(p, smem, tm, tn, k_begin, k_end, acc);
   epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, tm, tn, split);
 }
 
