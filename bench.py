@@ -124,7 +124,6 @@ class GpuStep:
             ws_bytes = max(ws_bytes, g.workspace_bytes(M, N, K))
             self.gemms.append(e)
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-        self.events = None
 
     def _q(self, mode, X, Q, s, ld):
         rows, cols = X.shape
