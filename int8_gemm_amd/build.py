@@ -52,6 +52,14 @@ def build(verbose: bool = False, asm_dir: str = None) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    # A kernel template whose host-side instantiation fails leaves its launch
+    # stub undefined: the link succeeds, but loading the library would not.
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        stubs = [l.split()[-1] for l in und.splitlines() if "__device_stub__" in l]
+        if stubs:
+            raise RuntimeError("undefined kernel launch stubs in the built library: " + ", ".join(stubs))
     os.replace(tmp, LIB_PATH)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)

@@ -116,6 +116,13 @@ __device__ __forceinline__ void dma_load16(const int8_t* g, int8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | (((N >> 4) & 3) << 14));
+}
+
 // Workgroup barrier without a memory fence (the fence of __syncthreads()
 // would wait for every outstanding global load, including prefetches).
 // Callers make the LDS data visible first: s_waitcnt on the counter that
@@ -887,6 +894,587 @@ gemm_i8_persist_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Persistent GEMM with 128-byte K stages.
+//
+// The tile walk and the drained epilogue of gemm_i8_persist_kernel, with a
+// schedule built around two measured properties of gfx950:
+//  * Direct-to-LDS loads cost per request.  Eight lanes fetching one whole
+//    128-byte line per row feed a CU about twice as fast as four lanes
+//    fetching half a line (about 56 against 29 bytes per clock per CU, all
+//    CUs loading).  A stage therefore holds 128 bytes of K per row, and the
+//    ring has three stages (120 KiB for a 128x192 tile).
+//  * With one wave per SIMD, every wait a wave takes leaves its matrix core
+//    idle.  A stage is four k-steps of six MFMAs per wave.  The fragment reads
+//    of k-step t+1 are issued during k-step t.  Four elements per k-step of the
+//    previous tile's epilogue block (one 32x32 block per stage), and the loads
+//    of stage g+2, are interleaved with the MFMAs.  The stage's only barrier
+//    sits between k-steps 1 and 2, and the scales and row keys that the next
+//    stage's epilogue block needs are read just before it.
+// LDS rows are 128 bytes.  Chunk c of row r is stored at position
+// c ^ ((r / 2) % 8), which puts the 16 lanes of each fragment read on
+// distinct banks.
+// Requires K % 128 == 0, K / 128 >= blocks per wave (FM * FN), M % BM == 0 (no
+// ragged tile-row: only columns are masked, through the buffer range check)
+// and ldc <= kPersistMaxLdc.
+// ---------------------------------------------------------------------------
+constexpr int BK2 = 128;   // bytes of K per stage of gemm_i8_persist128_kernel
+
+// The lane index, read so that the compiler can neither hoist it nor values
+// derived from it out of loops: per-lane addresses used once per stage are
+// then recomputed (two VALU operations) instead of being kept live across the
+// whole kernel, where register pressure would spill them to scratch (and a
+// scratch reload waits for every outstanding load of the LDS ring).
+__device__ __forceinline__ int lane_id_local() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+__device__ __forceinline__ int swz128(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// Buffer loads that write LDS directly: lane l's 16 (or 4) bytes land at
+// lds + 16*l (4*l); lds must be the same for the whole wave.  Offsets at or
+// beyond the resource's record count are not read.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
+gemm_i8_persist128_kernel(const GemmParams p) {
+  constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
+  static_assert(NWAVES == 4, "four waves, one per SIMD");
+  constexpr int STAGES = 3;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  // wave tiles of whole 32x32 blocks: every fragment row base is then a
+  // multiple of 32, which leaves the swizzle phase (row/2)%8 to the lane
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 blocks");
+  constexpr int FM = WTM / 32, FN = WTN / 32, NB = FM * FN;
+  static_assert(NB % 2 == 0, "epilogue operands alternate between two register sets");
+  constexpr int A_BYTES = BM * BK2, STAGE = (BM + BN) * BK2;
+  constexpr int A_INS = BM / (8 * NWAVES), B_INS = BN / (8 * NWAVES);   // 8 rows per load
+  static_assert(A_INS * 8 * NWAVES == BM && B_INS * 8 * NWAVES == BN, "rows per stage");
+  constexpr int LPS = A_INS + B_INS;                    // loads per wave per stage
+  constexpr int RING = STAGES * STAGE;
+  constexpr int SCL = BM + BN;                          // floats per scale slot: rows, then columns
+  constexpr int NSI = SCL / 64;                         // dword loads per scale slot
+  static_assert(NSI * 64 == SCL, "tile sides are multiples of 64");
+  constexpr int SQ = (NSI + NWAVES - 1) / NWAVES;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[RING + 3 * SCL * 4 + 3 * BM * 4 + 64];
+  float* const s_scl = reinterpret_cast<float*>(smem + RING);                              // [3][SCL]
+  unsigned int* const s_rk = reinterpret_cast<unsigned int*>(smem + RING + 3 * SCL * 4);  // [3][BM]
+  unsigned long long* const s_red =
+      reinterpret_cast<unsigned long long*>(smem + RING + 3 * SCL * 4 + 3 * BM * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int M = p.M, N = p.N;
+  const int nst = p.K / BK2;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int G = gridDim.x;
+  const int64_t ldc4 = p.ldc * 4;
+
+  // this workgroup's tiles (as in gemm_i8_persist_kernel)
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int per = G >> 3, rem = G & 7;
+  const int wpos = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int my_tiles = wpos < tiles ? (tiles - 1 - wpos) / G + 1 : 0;
+  auto tile_coords = [&](int r, int& tm, int& tn) __attribute__((always_inline)) {
+    const int n = r * G + wpos;
+    const int group_size = GROUP_M * p.tiles_n;
+    const int group = n / group_size;
+    const int first_m = group * GROUP_M;
+    const int gm = (p.tiles_m - first_m) < GROUP_M ? (p.tiles_m - first_m) : GROUP_M;
+    const int in_group = n - group * group_size;
+    tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
+    tn = __builtin_amdgcn_readfirstlane(in_group / gm);
+  };
+
+  // ---- direct-to-LDS loads: lane l of a load fills row l/8, position l%8 ----
+  const int r_in = lane >> 3, pch = lane & 7;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm_s = wave_s / WAVES_N, wn_s = wave_s % WAVES_N;
+  // Loads go through buffer resources: the tile (and stage) base is scalar,
+  // and each lane's offset is the same for every tile.  B rows at or beyond N
+  // and column scales at or beyond N fall outside the resource's range and
+  // read as zeros: their columns' stores are dropped and their hash keys are 0.
+  struct Src {
+    const int8_t* abase;   // A at the tile's first row
+    const int8_t* bbase;   // B at the tile's first row
+    const float* rbase;    // s_row at the tile's first row
+    const float* cbase;    // s_col at the tile's first column
+    int ncol;              // columns of the tile inside the matrix
+    int slot;              // scale slot of the tile
+  };
+  int a_off[A_INS], b_off[B_INS];
+#pragma unroll
+  for (int q = 0; q < A_INS; ++q) {
+    const int row = (q * NWAVES + wave) * 8 + r_in;
+    a_off[q] = row * (int)p.lda + (swz128(row, pch) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < B_INS; ++q) {
+    const int row = (q * NWAVES + wave) * 8 + r_in;
+    b_off[q] = row * (int)p.ldb + (swz128(row, pch) << 4);
+  }
+  const int lane4 = lane * 4;
+  auto make_src = [&](int r, int tm, int tn, Src& s) __attribute__((always_inline)) {
+    s.slot = __builtin_amdgcn_readfirstlane(r % 3);
+    const int row0 = tm * BM, col0 = tn * BN;
+    s.abase = uniform_ptr(p.A + (int64_t)row0 * p.lda);
+    s.bbase = uniform_ptr(p.B + (int64_t)col0 * p.ldb);
+    s.rbase = uniform_ptr(p.s_row + row0);
+    s.cbase = uniform_ptr(p.s_col + col0);
+    s.ncol = __builtin_amdgcn_readfirstlane(N - col0 < BN ? N - col0 : BN);
+  };
+  // The loads of one stage: LPS per wave, A's row blocks first, then B's.
+  struct Dma {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int8_t* base;
+  };
+  auto dma_setup = [&](int buf, const Src& s, int kt) __attribute__((always_inline)) {
+    Dma d;
+    d.base = smem + buf * STAGE + wave_s * 1024;
+    d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(s.abase + kt * BK2), 0, (int)kBufRecords,
+                                             0x00020000);
+    d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(s.bbase + kt * BK2), 0,
+                                             s.ncol * (int)p.ldb - kt * BK2, 0x00020000);
+    return d;
+  };
+  auto dma_range = [&](const Dma& d, auto LO, auto HI) __attribute__((always_inline)) {
+    static_for<decltype(LO)::value, decltype(HI)::value>([&](auto LI) __attribute__((always_inline)) {
+      constexpr int l = decltype(LI)::value;
+      if constexpr (l < A_INS)
+        buffer_load_lds16(d.ra, d.base + l * NWAVES * 1024, a_off[l]);
+      else
+        buffer_load_lds16(d.rb, d.base + A_BYTES + (l - A_INS) * NWAVES * 1024, b_off[l - A_INS]);
+    });
+  };
+  auto issue_ops = [&](int buf, const Src& s, int kt) __attribute__((always_inline)) {
+    dma_range(dma_setup(buf, s, kt), std::integral_constant<int, 0>(), std::integral_constant<int, LPS>());
+  };
+  // the tile's row and column scales into slot s.slot: load k (k = q*4 + wave)
+  // covers entries 64k .. 64k+63 of [rows | columns]
+  auto issue_scales = [&](const Src& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < SQ; ++q) {
+      const int k = q * NWAVES + wave_s;
+      if (k < NSI) {
+        __amdgpu_buffer_rsrc_t rs;
+        if (k * 64 < BM) {
+          rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s.rbase + k * 64), 0, 256, 0x00020000);
+        } else {
+          const int c0 = k * 64 - BM;
+          const int left = s.ncol - c0;
+          rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s.cbase + c0), 0,
+                                                 (left > 0 ? left : 0) * 4, 0x00020000);
+        }
+        buffer_load_lds4(rs, s_scl + s.slot * SCL + k * 64, lane4);
+      }
+    }
+  };
+
+  // ---- fragments: k-step t of a stage reads logical chunk 2t + lane/32 ----
+  // Row bases are multiples of 32 (A) or of WTN (B), which keep (row/2)%8 equal
+  // to (lrow/2)%8, so one per-lane chunk offset serves every fragment.
+  int kc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) kc[t] = lrow * BK2 + (swz128(lrow, 2 * t + lhalf) << 4);
+  const int a_row0 = wm * WTM * BK2, b_row0 = A_BYTES + wn * WTN * BK2;
+  v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto load_frags = [&](int buf, int t, v4i (&fa)[FM], v4i (&fb)[FN]) __attribute__((always_inline)) {
+    const int8_t* sb = smem + buf * STAGE + kc[t];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const v4i*>(sb + a_row0 + i * 32 * BK2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const v4i*>(sb + b_row0 + j * 32 * BK2);
+  };
+  v16i acc0[FM][FN], acc1[FM][FN];
+
+  // ---- epilogue of the tile being drained ----
+  struct Out {
+    float* cbase;          // C at the tile's first row
+    int voff[FN];          // this lane's column byte offset (+4 rows for lanes 32..63), or kBufInvalid
+    uint32_t sr_base;      // LDS address of this lane's first row scale of the wave's rows
+    uint32_t rk_base;      // LDS address of this lane's first row key of the wave's rows
+    uint32_t sc_base;      // LDS address of this lane's column scale in the wave's first block column
+    int col0;              // the tile's first column
+    int slot;              // scale / key slot of the tile
+  };
+  uint64_t tcol[FN];       // per-column hash sums of the tile being drained
+  uint64_t lane_hash = 0;  // this lane's share of S over every drained tile
+  auto make_out = [&](int r, int tm, int tn, Out& o) __attribute__((always_inline)) {
+    const int row0 = tm * BM;
+    o.cbase = uniform_ptr(p.C + (int64_t)row0 * p.ldc);
+    o.slot = __builtin_amdgcn_readfirstlane(r % 3);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = tn * BN + wn * WTN + j * 32 + lrow;
+      const bool ok = col < N;
+      o.voff[j] = ok ? (int)(lhalf * 4 * ldc4 + col * 4) : kBufInvalid;
+    }
+    o.col0 = tn * BN;
+    o.sr_base = lds_addr(s_scl + o.slot * SCL) + (wm * WTM + lhalf * 4) * 4;
+    o.rk_base = lds_addr(s_rk + o.slot * BM) + (wm * WTM + lhalf * 4) * 4;
+    o.sc_base = lds_addr(s_scl + o.slot * SCL + BM) + (wn * WTN + lrow) * 4;
+    for (int rr = tid; rr < BM; rr += NT) s_rk[o.slot * BM + rr] = hash_row_key((unsigned int)(row0 + rr));
+  };
+  // Scales and row keys of the epilogue blocks, read and waited for inside
+  // one asm statement each time (the compiler would otherwise wait for every
+  // outstanding direct-to-LDS load before reading LDS that such loads write).
+  // A half holds parts 2h and 2h+1 of a block: the row scales and row keys of
+  // this lane's rows 16h + 4*(lane/32) + {0..3, 8..11}.
+  struct DHalf {
+    v4i sr[2];
+    v4i rk[2];
+  };
+  // Byte offsets (immediates of the LDS reads): the row scales / keys of half
+  // h of block row i start 32i + 16h rows into the wave's rows; the column
+  // scale of block column j is 32j columns into the wave's columns.
+  auto read_late_early = [&](const Out& o1, auto B, DHalf& late, const Out& o2, auto C, DHalf& early,
+                             int& sc) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value, c = decltype(C)::value;
+    constexpr int ol = (b / FN) * 128 + 64, oe = (c / FN) * 128, oc = (c % FN) * 128;
+    asm volatile(
+        "ds_read_b128 %[l0], %[sr1] offset:%[ol0]\n\t"
+        "ds_read_b128 %[l1], %[sr1] offset:%[ol1]\n\t"
+        "ds_read_b128 %[l2], %[rk1] offset:%[ol0]\n\t"
+        "ds_read_b128 %[l3], %[rk1] offset:%[ol1]\n\t"
+        "ds_read_b128 %[e0], %[sr2] offset:%[oe0]\n\t"
+        "ds_read_b128 %[e1], %[sr2] offset:%[oe1]\n\t"
+        "ds_read_b128 %[e2], %[rk2] offset:%[oe0]\n\t"
+        "ds_read_b128 %[e3], %[rk2] offset:%[oe1]\n\t"
+        "ds_read_b32 %[sc], %[sc2] offset:%[oc]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [l0] "=&v"(late.sr[0]), [l1] "=&v"(late.sr[1]), [l2] "=&v"(late.rk[0]),
+          [l3] "=&v"(late.rk[1]), [e0] "=&v"(early.sr[0]), [e1] "=&v"(early.sr[1]),
+          [e2] "=&v"(early.rk[0]), [e3] "=&v"(early.rk[1]), [sc] "=&v"(sc)
+        : [sr1] "v"(o1.sr_base), [rk1] "v"(o1.rk_base), [sr2] "v"(o2.sr_base),
+          [rk2] "v"(o2.rk_base), [sc2] "v"(o2.sc_base), [ol0] "i"(ol), [ol1] "i"(ol + 32),
+          [oe0] "i"(oe), [oe1] "i"(oe + 32), [oc] "i"(oc));
+  };
+  // the second half of block b of o
+  auto read_late = [&](const Out& o, auto B, DHalf& late) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    constexpr int ol = (b / FN) * 128 + 64;
+    asm volatile(
+        "ds_read_b128 %[l0], %[sr] offset:%[o0]\n\t"
+        "ds_read_b128 %[l1], %[sr] offset:%[o1]\n\t"
+        "ds_read_b128 %[l2], %[rk] offset:%[o0]\n\t"
+        "ds_read_b128 %[l3], %[rk] offset:%[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [l0] "=&v"(late.sr[0]), [l1] "=&v"(late.sr[1]), [l2] "=&v"(late.rk[0]),
+          [l3] "=&v"(late.rk[1])
+        : [sr] "v"(o.sr_base), [rk] "v"(o.rk_base), [o0] "i"(ol), [o1] "i"(ol + 32));
+  };
+  // the first half and column scale of block c of o
+  auto read_early = [&](const Out& o, auto C, DHalf& early, int& sc) __attribute__((always_inline)) {
+    constexpr int c = decltype(C)::value;
+    constexpr int oe = (c / FN) * 128, oc = (c % FN) * 128;
+    asm volatile(
+        "ds_read_b128 %[e0], %[sr] offset:%[o0]\n\t"
+        "ds_read_b128 %[e1], %[sr] offset:%[o1]\n\t"
+        "ds_read_b128 %[e2], %[rk] offset:%[o0]\n\t"
+        "ds_read_b128 %[e3], %[rk] offset:%[o1]\n\t"
+        "ds_read_b32 %[sc], %[sca] offset:%[oc]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [e0] "=&v"(early.sr[0]), [e1] "=&v"(early.sr[1]), [e2] "=&v"(early.rk[0]),
+          [e3] "=&v"(early.rk[1]), [sc] "=&v"(sc)
+        : [sr] "v"(o.sr_base), [rk] "v"(o.rk_base), [sca] "v"(o.sc_base), [o0] "i"(oe),
+          [o1] "i"(oe + 32), [oc] "i"(oc));
+  };
+  // Element 4q+e of block b = (i, j) of accumulator set Y: lane l holds
+  // column l % 32 and row 8q + 4*(l/32) + e of the block.
+  auto drain_elem = [&](v16i (&Y)[FM][FN], const Out& o, const DHalf& d, int scb, auto IJ, auto Q, auto E)
+      __attribute__((always_inline)) {
+    constexpr int b = decltype(IJ)::value, q = decltype(Q)::value, e = decltype(E)::value;
+    constexpr int i = b / FN, j = b % FN;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(o.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
+        0x00020000);
+    float y = epilogue1(Y[i][j][q * 4 + e], __int_as_float(d.sr[q % 2][e]), __int_as_float(scb));
+    if (RELU) y = relu_pos0(y);
+    tcol[j] += (uint64_t)(unsigned int)d.rk[q % 2][e] * (uint64_t)__float_as_uint(y);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, o.voff[j], (q * 8 + e) * (int)ldc4, 0);
+    // keep the hash terms where they are computed: summed later, they would
+    // keep every y alive
+    if constexpr (e == 3) asm volatile("" : "+v"(tcol[j]));
+  };
+  // The four elements of part q of block b = (i, j), in steps spread over the
+  // slots of a k-step so that the four dependency chains overlap each other
+  // and the MFMAs: step 0 converts the accumulators, 1 applies the row
+  // scales, 2 the column scale (and ReLU), 3 adds the hash terms of elements
+  // 0-1 and stores them, 4 the same for elements 2-3.
+  float xq[4];
+  auto drain_step = [&](v16i (&Y)[FM][FN], const Out& o, const DHalf& d, int scb, auto IJ, auto Q,
+                        auto STEP) __attribute__((always_inline)) {
+    constexpr int b = decltype(IJ)::value, q = decltype(Q)::value, st = decltype(STEP)::value;
+    constexpr int i = b / FN, j = b % FN;
+    if constexpr (st == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xq[e] = (float)Y[i][j][q * 4 + e];
+    } else if constexpr (st == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xq[e] = mul_rn(xq[e], __int_as_float(d.sr[q % 2][e]));
+    } else if constexpr (st == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xq[e] = mul_rn(xq[e], __int_as_float(scb));
+        if (RELU) xq[e] = relu_pos0(xq[e]);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(o.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
+          0x00020000);
+      constexpr int e0 = (st - 3) * 2;
+#pragma unroll
+      for (int e = e0; e < e0 + 2; ++e) {
+        tcol[j] += (uint64_t)(unsigned int)d.rk[q % 2][e] * (uint64_t)__float_as_uint(xq[e]);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xq[e]), rsrc, o.voff[j], (q * 8 + e) * (int)ldc4, 0);
+      }
+      if constexpr (st == 4) asm volatile("" : "+v"(tcol[j]));
+    }
+  };
+  auto close_tile_hash = [&](const Out& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = o.col0 + wn * WTN + j * 32 + lrow;
+      lane_hash += (col < N ? hash_col_key((uint64_t)col) : 0ull) * tcol[j];
+      tcol[j] = 0;
+    }
+  };
+
+  // One k-step, laid out slot by slot (a scheduling fence after each): slot m
+  // issues MFMA m of X (fragments fa/fb); slots 0-2 read the next k-step's
+  // fragments (stage buffer nbuf, k-step nt) into na/nb; with a stage to
+  // fetch, slots 0-4 issue its loads; slot(m) adds the epilogue work of the
+  // slot.  Fixing the order keeps the two fragment sets in distinct registers
+  // and the reads one to five MFMAs ahead of their use.
+  constexpr int NSLOT = FM * FN;
+  constexpr int LPSL = (LPS + NSLOT - 2) / (NSLOT - 1);   // loads per slot, slots 0 .. NSLOT-2
+  auto kstep = [&](v16i (&X)[FM][FN], const v4i (&fa)[FM], const v4i (&fb)[FN], auto ZERO, int nbuf,
+                   int nt, v4i (&na)[FM], v4i (&nb)[FN], auto DMA, const Dma& dm, auto&& slot)
+      __attribute__((always_inline)) {
+    constexpr bool zero = decltype(ZERO)::value, dma = decltype(DMA)::value;
+    const int8_t* sb = smem + nbuf * STAGE + kc[nt];
+    static_for<0, NSLOT>([&](auto MI) __attribute__((always_inline)) {
+      constexpr int m = decltype(MI)::value, i = m / FN, j = m % FN;
+      X[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], zero ? v16i{} : X[i][j], 0, 0, 0);
+      constexpr int r0 = 2 * m, r1 = (2 * m + 2 < FM + FN) ? 2 * m + 2 : FM + FN;
+      static_for<r0, r1>([&](auto RI) __attribute__((always_inline)) {
+        constexpr int r = decltype(RI)::value;
+        if constexpr (r < FM)
+          na[r] = *reinterpret_cast<const v4i*>(sb + a_row0 + r * 32 * BK2);
+        else
+          nb[r - FM] = *reinterpret_cast<const v4i*>(sb + b_row0 + (r - FM) * 32 * BK2);
+      });
+      if constexpr (dma) {
+        constexpr int l0 = m * LPSL < LPS ? m * LPSL : LPS;
+        constexpr int l1 = (m + 1) * LPSL < LPS ? (m + 1) * LPSL : LPS;
+        dma_range(dm, std::integral_constant<int, l0>(), std::integral_constant<int, l1>());
+      }
+      slot(MI);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- the fetch cursor: the tile and stage whose loads are issued next ----
+  Src fsrc;
+  int fr = 0, fkt = 0;
+  auto advance_fetch = [&]() __attribute__((always_inline)) {
+    ++fkt;
+    if (fkt == nst) {
+      if (fr + 1 < my_tiles) {
+        ++fr;
+        int a, b;
+        tile_coords(fr, a, b);
+        make_src(fr, a, b, fsrc);
+        fkt = 0;
+        issue_scales(fsrc);
+      } else {
+        fkt = nst - 1;   // past the end: repeat a stage into a slot that is never read
+      }
+    }
+  };
+
+  // One stage g of tile r (tile-local position s).  X accumulates tile r.
+  // If DRAIN, block BLK of Y (tile r-1, Out oy) is drained: parts 0-1 with
+  // the operand half `early` (read during the previous stage), parts 2-3 with
+  // `late`, which mid() reads just before the barrier together with the next
+  // stage's early half.  ST: the stage's loads are waited for with this many
+  // later stores allowed outstanding (a lower bound of the stores issued
+  // after them: those of k-step 3 of the previous stage and of k-steps 0-1 of
+  // this one, counted only where those stages drain).
+  auto stage = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int g, const Out& oy, const DHalf& early,
+                   int scb, DHalf& late, auto FIRST, auto DRAIN, auto BLK, auto STV, auto&& mid)
+      __attribute__((always_inline)) {
+    constexpr bool D = decltype(DRAIN)::value;
+    constexpr int ST = decltype(STV)::value;
+    const int buf = g % STAGES;
+    // epilogue part q: steps 0-4 of its four elements in slots 0-4
+    auto part = [&](auto Q) __attribute__((always_inline)) {
+      return [&, Q](auto MI) __attribute__((always_inline)) {
+        constexpr int m = decltype(MI)::value, q = decltype(Q)::value;
+        if constexpr (D && m <= 4) {
+          if constexpr (q < 2)
+            drain_step(Y, oy, early, scb, BLK, Q, std::integral_constant<int, m>());
+          else
+            drain_step(Y, oy, late, scb, BLK, Q, std::integral_constant<int, m>());
+        }
+      };
+    };
+    const Dma none{};
+    kstep(X, fa0, fb0, FIRST, buf, 1, fa1, fb1, std::false_type(), none, part(std::integral_constant<int, 0>()));
+    kstep(X, fa1, fb1, std::false_type(), buf, 2, fa0, fb0, std::false_type(), none,
+          part(std::integral_constant<int, 1>()));
+    mid();   // epilogue operands (read and waited for)
+    kstep(X, fa0, fb0, std::false_type(), buf, 3, fa1, fb1, std::false_type(), none,
+          part(std::integral_constant<int, 2>()));
+    // This wave's reads of stage g are complete and stage g+1 has landed for
+    // it; after the barrier, for every wave: stage g's slot is free and
+    // stage g+1 can be read.
+    wait_vmcnt_lgkm0<ST>();
+    barrier_nofence();
+    // k-step 3 reads k-step 0 of stage g+1 and loads stage g+3 into stage g's slot
+    const Dma dm = dma_setup(buf, fsrc, fkt);
+    kstep(X, fa1, fb1, std::false_type(), (g + 1) % STAGES, 0, fa0, fb0, std::true_type(), dm,
+          part(std::integral_constant<int, 3>()));
+    advance_fetch();
+  };
+
+  // One tile r: X accumulates it; if DRAIN, Y (tile r-1, Out out_prev) is
+  // drained during its first NB stages.  The early halves alternate between
+  // (e0, s0) and (e1, s1); block 0 of a tile always uses (e0, s0).
+  DHalf e0, e1, late;
+  int s0 = 0, s1 = 0;
+  Out out_cur, out_prev;
+  auto run_tile = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int r, auto DRAIN)
+      __attribute__((always_inline)) {
+    constexpr bool D = decltype(DRAIN)::value;
+    const int g0 = r * nst;
+    const bool has_next = r + 1 < my_tiles;
+    static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
+      constexpr int b = decltype(BI)::value;
+      constexpr int ST = LPS + (D && b >= 1 ? 16 : 0) + (D ? 12 : 0);
+      DHalf& ec = (b % 2 == 0) ? e0 : e1;
+      DHalf& en = (b % 2 == 0) ? e1 : e0;
+      int& sc_c = (b % 2 == 0) ? s0 : s1;
+      int& sc_n = (b % 2 == 0) ? s1 : s0;
+      auto mid = [&]() __attribute__((always_inline)) {
+        if constexpr (D && b + 1 < NB) {
+          read_late_early(out_prev, BI, late, out_prev, std::integral_constant<int, b + 1>(), en, sc_n);
+        } else if constexpr (D) {
+          // last block; if nst == NB the next stage is the next tile's first,
+          // which drains block 0 of this tile
+          if (nst == NB && has_next)
+            read_late_early(out_prev, BI, late, out_cur, std::integral_constant<int, 0>(), en, sc_n);
+          else
+            read_late(out_prev, BI, late);
+        } else if constexpr (b + 1 == NB) {
+          if (nst == NB && has_next) read_early(out_cur, std::integral_constant<int, 0>(), en, sc_n);
+        }
+      };
+      stage(X, Y, g0 + b, out_prev, ec, sc_c, late, std::integral_constant<bool, b == 0>(), DRAIN, BI,
+            std::integral_constant<int, ST>(), mid);
+    });
+    if (D) close_tile_hash(out_prev);
+    static_assert(NB % 2 == 0, "stage NB (if any) finds its next early half in e0");
+    for (int s = NB; s < nst; ++s) {
+      auto mid = [&]() __attribute__((always_inline)) {
+        if (s + 1 == nst && has_next) read_early(out_cur, std::integral_constant<int, 0>(), e0, s0);
+      };
+      if (s == NB)
+        stage(X, Y, g0 + s, out_prev, e0, s0, late, std::false_type(), std::false_type(),
+              std::integral_constant<int, 0>(), std::integral_constant<int, LPS + (D ? 16 : 0)>(), mid);
+      else
+        stage(X, Y, g0 + s, out_prev, e0, s0, late, std::false_type(), std::false_type(),
+              std::integral_constant<int, 0>(), std::integral_constant<int, LPS>(), mid);
+    }
+  };
+
+  if (my_tiles > 0) {
+    int tm, tn;
+    tile_coords(0, tm, tn);
+    make_src(0, tm, tn, fsrc);
+    make_out(0, tm, tn, out_cur);
+    // prologue: scales and the first three stages of tile 0
+    issue_scales(fsrc);
+    issue_ops(0, fsrc, 0);
+    issue_ops(1, fsrc, 1);
+    issue_ops(2, fsrc, 2);
+    fkt = 3;   // nst >= NB >= 3
+    wait_vmcnt_lgkm0<2 * LPS>();   // stage 0 landed; the row keys of tile 0 written
+    barrier_nofence();
+    load_frags(0, 0, fa0, fb0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) tcol[j] = 0;
+
+    run_tile(acc0, acc1, 0, std::false_type());
+    for (int r = 1; r < my_tiles; ++r) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc1[i][j] = acc0[i][j];
+      out_prev = out_cur;
+      int a, b;
+      tile_coords(r, a, b);
+      make_out(r, a, b, out_cur);
+      run_tile(acc0, acc1, r, std::true_type());
+    }
+    // The last tile: no MFMAs left to hide its epilogue under.  Its hash
+    // terms come first and its stores last, so that publishing this
+    // workgroup's share of S (whose acknowledgement the ticket waits for,
+    // and vmcnt retires in order) does not wait behind the tile's stores.
+    // Every direct-to-LDS load has landed here, so plain LDS reads are used.
+    wait_vmcnt<0>();
+    if (p.do_hash) {
+      static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
+        constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
+        const int r0 = wm * WTM + i * 32 + lhalf * 4;
+        const float* srp = s_scl + out_cur.slot * SCL + r0;
+        const unsigned int* rkp = s_rk + out_cur.slot * BM + r0;
+        const float sc = s_scl[out_cur.slot * SCL + BM + wn * WTN + j * 32 + lrow];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = (v >> 2) * 8 + (v & 3);
+          float y = epilogue1(acc0[i][j][v], srp[rr], sc);
+          if (RELU) y = relu_pos0(y);
+          tcol[j] += (uint64_t)rkp[rr] * (uint64_t)__float_as_uint(y);
+        }
+      });
+      close_tile_hash(out_cur);
+    }
+  }
+  if (p.do_hash) {
+    const uint64_t part = block_sum_u64<NT>(lane_hash, s_red);
+    hash_share_and_finalize<NT>(part, p.hash_parts, p.ticket, p.n_shares, blockIdx.x, (uint64_t)M,
+                                (uint64_t)N, p.hash_out, s_red, reinterpret_cast<int*>(s_red + NWAVES));
+  }
+  if (my_tiles > 0) {
+    static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
+      constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
+      const int r0 = wm * WTM + i * 32 + lhalf * 4;
+      const float* srp = s_scl + out_cur.slot * SCL + r0;
+      const float sc = s_scl[out_cur.slot * SCL + BM + wn * WTN + j * 32 + lrow];
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(out_cur.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
+          0x00020000);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = (v >> 2) * 8 + (v & 3);
+        float y = epilogue1(acc0[i][j][v], srp[rr], sc);
+        if (RELU) y = relu_pos0(y);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, out_cur.voff[j], rr * (int)ldc4, 0);
+      }
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
 // split-K combine: acc = sum over splits (exact), then the same epilogue and
 // hash shares as the GEMM kernel; each thread owns 4 consecutive columns of a
 // band of p.comb_rows rows (chosen so that the grid has about a thousand
@@ -975,16 +1563,18 @@ struct TileCfg {
   double wg_out_bw;      // bytes/s of output one workgroup writes in its epilogue
   double tile_overhead;  // persistent: seconds per tile beyond its MACs
   bool persistent;       // one workgroup per CU walking tiles, epilogue drained under the next tile
+  int kstage;            // bytes of K per LDS stage
 };
 static const TileCfg kCfgs[] = {
-    {256, 256, 1, 4.5e12, 20e9, 0, false},    // eight waves (two per SIMD), 128x64 each
-    {256, 128, 1, 3.3e12, 9.8e9, 0, false},   // four waves, 128x64 each
-    {128, 128, 2, 1.43e12, 6.9e9, 0, false},  // four waves, 64x64 each
-    {256, 256, 1, 4.0e12, 20e9, 0, false},    // four waves, 128x128 each (tests only)
-    {256, 128, 1, 3.0e12, 0, 6.0e-6, true},   // persistent, 128x64 per wave (tests only)
-    {128, 192, 1, 3.0e12, 0, 5.2e-6, true},   // persistent, four waves, 64x96 each
+    {256, 256, 1, 4.5e12, 20e9, 0, false, 64},    // eight waves (two per SIMD), 128x64 each
+    {256, 128, 1, 3.3e12, 9.8e9, 0, false, 64},   // four waves, 128x64 each
+    {128, 128, 2, 1.43e12, 6.9e9, 0, false, 64},  // four waves, 64x64 each
+    {256, 256, 1, 4.0e12, 20e9, 0, false, 64},    // four waves, 128x128 each (tests only)
+    {256, 128, 1, 3.0e12, 0, 6.0e-6, true, 64},   // persistent, 128x64 per wave (tests only)
+    {128, 192, 1, 3.0e12, 0, 5.2e-6, true, 64},   // persistent, four waves, 64x96 each
+    {128, 192, 1, 3.7e12, 0, 5.5e-6, true, 128},  // persistent, 128-byte stages, 64x96 per wave
 };
-constexpr int kNumCfgs = 6;
+constexpr int kNumCfgs = 7;
 constexpr int kPersistStages = 4;
 
 // Compute units of the current device (cached per device).
@@ -1028,8 +1618,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
     const int64_t tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const int64_t tiles = tm * tn;
     if (t.persistent) {
-      if (!allow_persistent || K % BK != 0 || kstages < kPersistStages - 1 || tiles > INT32_MAX / 2)
-        continue;
+      if (!allow_persistent || tiles > INT32_MAX / 2) continue;
+      if (t.kstage == BK && (K % BK != 0 || kstages < kPersistStages - 1)) continue;
+      // 128-byte stages: at least one stage per 32x32 block of a wave (64x96
+      // wave tiles: 6), and no ragged tile-row
+      if (t.kstage == BK2 && (K % BK2 != 0 || K / BK2 < 6 || M % t.bm != 0)) continue;
       if (force_splits > 1) continue;
       const int64_t grid = tiles < cus ? tiles : cus;
       const double rounds = std::ceil((double)tiles / (double)grid);
@@ -1044,7 +1637,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
         best.tiles_m = (int)tm;
         best.tiles_n = (int)tn;
         best.splits = 1;
-        best.k_per_split = (int)(kstages * BK);
+        best.k_per_split = (int)K;
         best.grid = (int)grid;
         best.persistent = true;
       }
@@ -1123,11 +1716,17 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
       else
         hipLaunchKernelGGL((gemm_i8_persist_kernel<256, 128, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
       break;
-    default:
+    case 5:
       if (p.relu)
         hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, true>), dim3(grid), dim3(256), 0, stream, p);
       else
         hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+    default:
+      if (p.relu)
+        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, true>), dim3(grid), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, false>), dim3(grid), dim3(256), 0, stream, p);
       break;
   }
   if (plan.splits > 1)
