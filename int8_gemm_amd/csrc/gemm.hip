@@ -938,6 +938,9 @@ __device__ __forceinline__ int swz128(int row, int chunk) { return chunk ^ ((row
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
+__device__ __forceinline__ int buffer_atomic_add_ret(__amdgpu_buffer_rsrc_t r, int v, int voff) {
+  return __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(v, r, voff, 0, 0);
+}
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
@@ -1352,6 +1355,13 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   DHalf e0, e1, late;
   int s0 = 0, s1 = 0;
   Out out_cur, out_prev;
+  // a workgroup without tiles stores nothing: every offset lies outside the range
+  out_cur.cbase = p.C;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) out_cur.voff[j] = kBufInvalid;
+  out_cur.sr_base = out_cur.rk_base = out_cur.sc_base = 0;
+  out_cur.col0 = 0;
+  out_cur.slot = 0;
   auto run_tile = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int r, auto DRAIN)
       __attribute__((always_inline)) {
     constexpr bool D = decltype(DRAIN)::value;
@@ -1449,28 +1459,69 @@ gemm_i8_persist128_kernel(const GemmParams p) {
       close_tile_hash(out_cur);
     }
   }
-  if (p.do_hash) {
-    const uint64_t part = block_sum_u64<NT>(lane_hash, s_red);
-    hash_share_and_finalize<NT>(part, p.hash_parts, p.ticket, p.n_shares, blockIdx.x, (uint64_t)M,
-                                (uint64_t)N, p.hash_out, s_red, reinterpret_cast<int*>(s_red + NWAVES));
-  }
-  if (my_tiles > 0) {
-    static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
-      constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
-      const int r0 = wm * WTM + i * 32 + lhalf * 4;
-      const float* srp = s_scl + out_cur.slot * SCL + r0;
-      const float sc = s_scl[out_cur.slot * SCL + BM + wn * WTN + j * 32 + lrow];
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(out_cur.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
-          0x00020000);
+  // The grid-wide sum of S (see hash_share_and_finalize), with its two
+  // round trips to the coherence point overlapped with the last tile's
+  // stores: thread 0 stores this workgroup's share; wave 0 then issues the
+  // stores of the first half of its blocks (vmcnt retires in order, so
+  // waiting until at most those stores are outstanding means the share is
+  // acknowledged), takes its ticket, and issues the second half before it
+  // needs the ticket's value.
+  constexpr int HALF = NB / 2;
+  auto store_block = [&](auto BI) __attribute__((always_inline)) {
+    constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
+    const int r0 = wm * WTM + i * 32 + lhalf * 4;
+    const float* srp = s_scl + out_cur.slot * SCL + r0;
+    const float sc = s_scl[out_cur.slot * SCL + BM + wn * WTN + j * 32 + lrow];
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(out_cur.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
+        0x00020000);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = (v >> 2) * 8 + (v & 3);
-        float y = epilogue1(acc0[i][j][v], srp[rr], sc);
-        if (RELU) y = relu_pos0(y);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, out_cur.voff[j], rr * (int)ldc4, 0);
+    for (int v = 0; v < 16; ++v) {
+      const int rr = (v >> 2) * 8 + (v & 3);
+      float y = epilogue1(acc0[i][j][v], srp[rr], sc);
+      if (RELU) y = relu_pos0(y);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, out_cur.voff[j], rr * (int)ldc4, 0);
+    }
+  };
+  // The share store and the ticket are issued by every lane of every wave,
+  // with offsets outside their buffers (dropped stores, no-op atomics) for
+  // all but thread 0: no branch, so the ticket's value is waited for only
+  // where it is used.
+  uint64_t part = 0;
+  if (p.do_hash) part = block_sum_u64<NT>(lane_hash, s_red);   // ends with a barrier
+  const bool t0h = p.do_hash && tid == 0;
+  {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(p.hash_parts), 0, (int)kBufRecords, 0x00020000);
+    const v2u pv = {(unsigned int)part, (unsigned int)(part >> 32)};
+    __builtin_amdgcn_raw_buffer_store_b64(pv, rs, t0h ? (int)blockIdx.x * 8 : kBufInvalid, 0, 16 /* sc1 */);
+  }
+  asm volatile("" ::: "memory");
+  static_for<0, HALF>(store_block);
+  asm volatile("" ::: "memory");
+  wait_vmcnt<HALF * 16>();   // the share store has been acknowledged
+  const __amdgpu_buffer_rsrc_t rt =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.ticket), 0, (int)kBufRecords, 0x00020000);
+  const unsigned int ticket = (unsigned int)buffer_atomic_add_ret(rt, 1, t0h ? 0 : kBufInvalid);
+  asm volatile("" ::: "memory");
+  static_for<HALF, NB>(store_block);
+  asm volatile("" ::: "memory");
+  if (p.do_hash) {
+    int* flag = reinterpret_cast<int*>(s_red + NWAVES);
+    if (threadIdx.x == 0) *flag = (ticket == (unsigned int)(p.n_shares - 1));
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only: the flag is written
+    barrier_nofence();
+    if (*flag) {   // the last workgroup: every other share is complete
+      uint64_t t = 0;
+      for (int k = tid; k < p.n_shares; k += NT)
+        t += __hip_atomic_load(p.hash_parts + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = block_sum_u64<NT>(t, s_red);
+      if (threadIdx.x == 0) {
+        *p.hash_out = hash_finalize(t, (uint64_t)M, (uint64_t)N);
+        __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-    });
+    }
   }
 }
 
