@@ -63,6 +63,8 @@ extern "C" {
                            /* aligned, or ld below K rounded up to 16        */
 #define I8G_EWORKSPACE  4  /* workspace missing, misaligned or too small     */
 #define I8G_EHIP        5  /* the HIP runtime reported a launch error        */
+#define I8G_EGATE       6  /* i8g_gate: a device output differs from the     */
+                           /* exact host mirror (see i8g_gate_report)        */
 
 /* flags of gemm_i8_blockscaled */
 #define I8G_RELU 1u        /* fused ReLU: out = out > 0 ? out : +0          */
@@ -166,6 +168,102 @@ size_t output_hash_workspace_bytes(void);
 int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
                 uint64_t* hash, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Self-checks, after the defence layers of the page "Verification -- why
+ * you can trust the numbers" ("Layer 1: exact init gates", "Layer 2:
+ * continuous audit", "Layer 3: the kernel probe").  Where that page falls
+ * back to a CPU mirror on a failed gate, this library refuses (I8G_EGATE):
+ * no entry point ever computes its outputs on the CPU.
+ * ------------------------------------------------------------------------ */
+
+/* Result of i8g_gate (host memory, filled by the call). */
+typedef struct i8g_gate_report {
+  int32_t check;     /* 0 = passed; 1 quantize_rows, 2 quantize_cols,
+                        3 GEMM output, 4 output hash (fused or standalone),
+                        5 the gate's inputs separate no wrong specification
+                        (index = which one: 0 round-half-even quantize,
+                        1 fused multiply-add quantize, 2 column scale first,
+                        3 scales multiplied first, 4 ReLU's +0)            */
+  int32_t config;    /* GEMM tile configuration that failed, or -1         */
+  int64_t m, n, k;   /* shape of the failing case (rows, cols for quantize) */
+  int64_t index;     /* first differing element (row-major), line, or -1   */
+  uint32_t got, want;/* bit patterns at that element (low 32 bits of a hash) */
+  int32_t cases;     /* number of cases that passed                         */
+} i8g_gate_report;
+
+/* Bytes of workspace i8g_gate needs (a constant, 16 MiB). */
+size_t i8g_gate_workspace_bytes(void);
+
+/*
+ * i8g_gate -- init gate: runs quantize_rows and quantize_cols (row and
+ * column passes, a long row, a tall column pass), the GEMM in every tile
+ * configuration of the planner (ReLU on and off, a split K) and the fused
+ * and standalone output hash on ragged shapes, and compares every output bit
+ * with an exact host mirror of the method built into the library.  The
+ * inputs hold exact ties x*inv = k + 0.5 and products just below 0.5 (where
+ * round-half-even and a fused multiply-add quantize differ from the method),
+ * and the gate checks that its GEMM outputs also separate the method from a
+ * column-scale-first or combined-scale epilogue and ReLU's +0 from -0; a
+ * pass therefore means the device follows the method where wrong
+ * specifications differ.  Floating-point behaviour is runtime state on a
+ * GPU, so run it at every start.
+ *   workspace  device scratch of i8g_gate_workspace_bytes(), 256-byte
+ *              aligned, any contents.
+ *   report     host pointer (may be NULL): which check failed and where.
+ * Unlike the other calls it copies data between host and device and
+ * synchronizes `stream`; it takes ~0.1-0.3 s of host time.
+ * Returns I8G_OK, I8G_EGATE (mismatch), I8G_EWORKSPACE or I8G_EHIP.
+ */
+int i8g_gate(void* workspace, size_t workspace_bytes, void* stream, i8g_gate_report* report);
+
+/*
+ * i8g_audit_gemm -- live audit of one GEMM output: `samples` cells (i, j),
+ * drawn from SplitMix64(seed), are recomputed on the device with a scalar
+ * dot product (not the MFMA path) and the epilogue, and compared bit for bit
+ * with C.  Arguments as gemm_i8_blockscaled (I8G_HASH in flags is ignored).
+ *   result  device pointer to two uint64_t: result[0] = number of sampled
+ *           cells that differ, result[1] = smallest i*N + j among them
+ *           (UINT64_MAX if none).  Written by the call's own kernels.
+ * Errors: I8G_EINVAL, I8G_EALIGN, I8G_EHIP.
+ */
+int i8g_audit_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,
+                   int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K,
+                   const float* C, int64_t ldc, uint32_t flags, uint64_t seed,
+                   int32_t samples, uint64_t* result, void* stream);
+
+/*
+ * i8g_audit_quantize -- live audit of a quantize pass: `samples` lines
+ * (rows of X for by_col == 0, checked against quantize_rows' Q and scale;
+ * columns for by_col == 1, against quantize_cols' Qt and scale), drawn from
+ * SplitMix64(seed), have their scale and every code recomputed.
+ *   result  as i8g_audit_gemm, with result[1] = smallest differing line.
+ * Errors: I8G_EINVAL, I8G_EHIP.
+ */
+int i8g_audit_quantize(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Q,
+                       int64_t ldq, const float* scale, int32_t by_col, uint64_t seed,
+                       int32_t samples, uint64_t* result, void* stream);
+
+/* Bytes of workspace i8g_probe_hash needs for this shape. */
+size_t i8g_probe_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * i8g_probe_hash -- the kernel probe: a seeded GEMM through the live kernels.
+ * A (M x K) and B (K x N), both row-major, take the outputs of SplitMix64
+ * seeded with `seed` in order, A first: output z becomes the binary32 value
+ * ((z >> 40) - 2^23) / 2^21, in [-4, 4).  SplitMix64 (Steele, Lea and Flood,
+ * 2014): output k is mix(seed + (k+1) * 0x9E3779B97F4A7C15) with
+ * mix(z) = z ^= z >> 30, z *= 0xBF58476D1CE4E5B9, z ^= z >> 27,
+ * z *= 0x94D049BB133111EB, z ^= z >> 31.  Then quantize_rows(A),
+ * quantize_cols(B) and gemm_i8_blockscaled (no ReLU) with its hash, which is
+ * written to *hash: every device that follows the method writes the same
+ * value.  M, N <= 2^20, K <= I8G_K_MAX.
+ *   workspace  device scratch of i8g_probe_workspace_bytes(M, N, K),
+ *              256-byte aligned, any contents.
+ * Errors: I8G_EINVAL, I8G_EWORKSPACE, I8G_EHIP.
+ */
+int i8g_probe_hash(uint64_t seed, int64_t M, int64_t N, int64_t K, uint64_t* hash,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* i8g_status_string(int status);

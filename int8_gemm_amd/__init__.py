@@ -30,7 +30,9 @@ I8G_RELU = 1
 I8G_HASH = 2
 K_MAX = 133144
 EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_workspace_bytes",
-            "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version")
+            "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version",
+            "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
+            "i8g_probe_hash", "i8g_probe_workspace_bytes")
 
 _lib = None
 _ws = {}
@@ -73,6 +75,20 @@ def load():
     lib.i8g_status_string.restype = ctypes.c_char_p
     lib.i8g_version.argtypes = []
     lib.i8g_version.restype = ctypes.c_char_p
+    lib.i8g_gate_workspace_bytes.argtypes = []
+    lib.i8g_gate_workspace_bytes.restype = c_sz
+    lib.i8g_gate.argtypes = [c_vp, c_sz, c_vp, ctypes.POINTER(GateReport)]
+    lib.i8g_gate.restype = ctypes.c_int
+    lib.i8g_audit_gemm.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp,
+                                   c_i64, c_u32, ctypes.c_uint64, ctypes.c_int32, c_vp, c_vp]
+    lib.i8g_audit_gemm.restype = ctypes.c_int
+    lib.i8g_audit_quantize.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, ctypes.c_int32,
+                                       ctypes.c_uint64, ctypes.c_int32, c_vp, c_vp]
+    lib.i8g_audit_quantize.restype = ctypes.c_int
+    lib.i8g_probe_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
+    lib.i8g_probe_workspace_bytes.restype = c_sz
+    lib.i8g_probe_hash.argtypes = [ctypes.c_uint64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    lib.i8g_probe_hash.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -188,6 +204,67 @@ def output_hash(C):
     ws = _workspace(C.device, int(load().output_hash_workspace_bytes()))
     _check(load().output_hash(_ptr(C), M, N, max(C.stride(0), N, 1), _ptr(h),
                               ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(C)))
+    return h
+
+
+class GateReport(ctypes.Structure):
+    """i8g_gate_report (include/int8_gemm.h)."""
+    _fields_ = [("check", ctypes.c_int32), ("config", ctypes.c_int32), ("m", ctypes.c_int64),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("index", ctypes.c_int64),
+                ("got", ctypes.c_uint32), ("want", ctypes.c_uint32), ("cases", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+def gate(device=None):
+    """Runs the init gate (i8g_gate) on `device` (default: the current one).
+    Returns (status, report dict); status 0 means every check passed."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    lib = load()
+    nbytes = int(lib.i8g_gate_workspace_bytes())
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rep = GateReport()
+    with torch.cuda.device(dev):
+        rc = lib.i8g_gate(ctypes.c_void_p(ws.data_ptr()), nbytes,
+                          ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(rep))
+    return rc, rep.as_dict()
+
+
+def audit_gemm(QA, s_row, QBt, s_col, C, relu=False, seed=0, samples=1024):
+    """i8g_audit_gemm on a GEMM output: returns a 2-element int64 device
+    tensor (number of differing sampled cells, smallest i*N + j of them or -1)."""
+    M, K = QA.shape
+    N = QBt.shape[0]
+    r = torch.empty(2, dtype=torch.int64, device=C.device)
+    _check(load().i8g_audit_gemm(
+        _ptr(QA), QA.stride(0) if M > 0 else _round16(K), _ptr(s_row), _ptr(QBt),
+        QBt.stride(0) if N > 0 else _round16(K), _ptr(s_col), M, N, K, _ptr(C), max(C.stride(0), N, 1),
+        I8G_RELU if relu else 0, seed & ((1 << 64) - 1), samples, _ptr(r), _stream(C)))
+    return r
+
+
+def audit_quantize(X, Q, scale, by_col, seed=0, samples=64):
+    """i8g_audit_quantize: X with its quantize_rows (by_col=False) or
+    quantize_cols (by_col=True) output; returns as audit_gemm (lines)."""
+    rows, cols = X.shape
+    r = torch.empty(2, dtype=torch.int64, device=X.device)
+    _check(load().i8g_audit_quantize(
+        _ptr(X), rows, cols, max(X.stride(0), cols, 1), _ptr(Q), max(Q.stride(0), 1), _ptr(scale),
+        1 if by_col else 0, seed & ((1 << 64) - 1), samples, _ptr(r), _stream(X)))
+    return r
+
+
+def probe_hash(seed, M, N, K, device=None):
+    """i8g_probe_hash: the output hash of the seeded probe GEMM (int64 tensor)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    lib = load()
+    nbytes = int(lib.i8g_probe_workspace_bytes(M, N, K))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    h = torch.zeros(1, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.i8g_probe_hash(seed & ((1 << 64) - 1), M, N, K, _ptr(h), ctypes.c_void_p(ws.data_ptr()),
+                                  nbytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
     return h
 
 

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libint8_gemm.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "hash.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "hash.hip", "verify.hip"]
 ARCH = "gfx950"
 
 

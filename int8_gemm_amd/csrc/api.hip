@@ -28,6 +28,69 @@ int check_quantize_args(const float* X, int64_t rows, int64_t cols, int64_t ldx,
 
 }  // namespace
 
+namespace i8g {
+
+int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt, int64_t ldb,
+                 const float* s_col, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
+                 uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream, int force_tile, int force_splits) {
+  if (M < 0 || N < 0 || K < 0) return I8G_EINVAL;
+  if (M > INT32_MAX || N > INT32_MAX) return I8G_EINVAL;
+  if (flags & ~(I8G_RELU | I8G_HASH)) return I8G_EINVAL;
+  const bool want_hash = (flags & I8G_HASH) != 0;
+  if (want_hash && !hash) return I8G_EINVAL;
+  if (K > I8G_K_MAX) return I8G_EKRANGE;
+  if (!workspace || ((uintptr_t)workspace % 256) != 0) return I8G_EWORKSPACE;
+  if (M == 0 || N == 0) {
+    if (workspace_bytes < kWsHeader) return I8G_EWORKSPACE;
+    if (want_hash) return hip_status(launch_output_hash(C, M, N, ldc, hash, workspace, stream));
+    return I8G_OK;
+  }
+  if (!C || !s_row || !s_col || ldc < N) return I8G_EINVAL;
+  if (K > 0 && (!QA || !QBt)) return I8G_EINVAL;
+  const int64_t k16 = (K + 15) / 16 * 16;
+  if (K > 0) {
+    if (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < k16 ||
+        ldb < k16)
+      return I8G_EALIGN;
+  }
+  // force_tile == -2: the library's own choice (plan_gemm, which honours the
+  // test overrides); otherwise exactly the forced configuration
+  GemmPlan plan = force_tile == -2
+                      ? plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc)
+                      : plan_gemm_forced(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc, force_tile, force_splits);
+  if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
+  GemmParams p;
+  p.A = QA;
+  p.B = QBt;
+  p.s_row = s_row;
+  p.s_col = s_col;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = plan.tiles_m;
+  p.tiles_n = plan.tiles_n;
+  p.splits = plan.splits;
+  p.k_per_split = plan.k_per_split;
+  p.relu = (flags & I8G_RELU) ? 1 : 0;
+  p.do_hash = want_hash ? 1 : 0;
+  p.stream_out = ((double)M * (double)N * 4.0 > 128.0 * 1024 * 1024) ? 1 : 0;
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.ticket = reinterpret_cast<unsigned int*>(ws);
+  p.hash_parts = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
+  p.n_shares = plan.hash_parts;
+  p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
+  p.comb_rows = plan.comb_rows;
+  p.hash_out = hash;
+  return hip_status(launch_gemm(p, plan, stream));
+}
+
+}  // namespace i8g
+
 extern "C" {
 
 const char* i8g_status_string(int status) {
@@ -38,6 +101,7 @@ const char* i8g_status_string(int status) {
     case I8G_EALIGN: return "GEMM operand not 16-byte aligned, or its leading dimension is not a multiple of 16 at least K rounded up to 16";
     case I8G_EWORKSPACE: return "workspace missing, misaligned or smaller than gemm_i8_workspace_bytes()";
     case I8G_EHIP: return "HIP runtime error while enqueueing a kernel";
+    case I8G_EGATE: return "self-check failed: a device output differs from the exact host mirror";
     default: return "unknown status";
   }
 }
@@ -76,55 +140,8 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
                         int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K, float* C,
                         int64_t ldc, uint32_t flags, uint64_t* hash, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (M < 0 || N < 0 || K < 0) return I8G_EINVAL;
-  if (M > INT32_MAX || N > INT32_MAX) return I8G_EINVAL;
-  if (flags & ~(I8G_RELU | I8G_HASH)) return I8G_EINVAL;
-  const bool want_hash = (flags & I8G_HASH) != 0;
-  if (want_hash && !hash) return I8G_EINVAL;
-  if (K > I8G_K_MAX) return I8G_EKRANGE;
-  if (!workspace || ((uintptr_t)workspace % 256) != 0) return I8G_EWORKSPACE;
-  if (M == 0 || N == 0) {
-    if (workspace_bytes < kWsHeader) return I8G_EWORKSPACE;
-    if (want_hash) return hip_status(launch_output_hash(C, M, N, ldc, hash, workspace, as_stream(stream)));
-    return I8G_OK;
-  }
-  if (!C || !s_row || !s_col || ldc < N) return I8G_EINVAL;
-  if (K > 0 && (!QA || !QBt)) return I8G_EINVAL;
-  const int64_t k16 = (K + 15) / 16 * 16;
-  if (K > 0) {
-    if (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < k16 ||
-        ldb < k16)
-      return I8G_EALIGN;
-  }
-  GemmPlan plan = plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc);
-  if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
-  GemmParams p;
-  p.A = QA;
-  p.B = QBt;
-  p.s_row = s_row;
-  p.s_col = s_col;
-  p.C = C;
-  p.lda = lda;
-  p.ldb = ldb;
-  p.ldc = ldc;
-  p.M = (int)M;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.tiles_m = plan.tiles_m;
-  p.tiles_n = plan.tiles_n;
-  p.splits = plan.splits;
-  p.k_per_split = plan.k_per_split;
-  p.relu = (flags & I8G_RELU) ? 1 : 0;
-  p.do_hash = want_hash ? 1 : 0;
-  p.stream_out = ((double)M * (double)N * 4.0 > 128.0 * 1024 * 1024) ? 1 : 0;
-  char* ws = reinterpret_cast<char*>(workspace);
-  p.ticket = reinterpret_cast<unsigned int*>(ws);
-  p.hash_parts = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
-  p.n_shares = plan.hash_parts;
-  p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
-  p.comb_rows = plan.comb_rows;
-  p.hash_out = hash;
-  return hip_status(launch_gemm(p, plan, as_stream(stream)));
+  return enqueue_gemm(QA, lda, s_row, QBt, ldb, s_col, M, N, K, C, ldc, flags, hash, workspace,
+                      workspace_bytes, as_stream(stream), -2, 0);
 }
 
 int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* hash, void* workspace,

@@ -1651,10 +1651,14 @@ static int env_int(const char* name, int dflt) {
 }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
+  return plan_gemm_forced(M, N, K, allow_persistent, env_int("I8G_FORCE_TILE", -1),
+                          env_int("I8G_FORCE_SPLITS", 0));
+}
+
+GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent, int force_tile,
+                          int force_splits) {
   GemmPlan best{};
   if (M <= 0 || N <= 0) return best;
-  const int force_tile = env_int("I8G_FORCE_TILE", -1);
-  const int force_splits = env_int("I8G_FORCE_SPLITS", 0);
   const int cus = device_cus();
   // Estimated seconds (see TileCfg), plus the split-K partial round trip;
   // no plan beats the whole output written at ~5 TB/s.

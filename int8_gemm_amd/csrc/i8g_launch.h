@@ -46,6 +46,18 @@ struct GemmPlan {
 constexpr int64_t kPersistMaxLdc = int64_t(1) << 23;
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent);
+// The same with the tile configuration and split count forced (-1 / 0: the
+// cost model's choice); a configuration that cannot run the shape falls back
+// to the 128x128 tile.  plan_gemm reads them from I8G_FORCE_TILE /
+// I8G_FORCE_SPLITS (tests only).
+GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent, int force_tile,
+                          int force_splits);
+// Validates, plans and enqueues one GEMM exactly as gemm_i8_blockscaled does
+// (force_tile / force_splits as in plan_gemm_forced).
+int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt, int64_t ldb,
+                 const float* s_col, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
+                 uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream, int force_tile, int force_splits);
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
 
 hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,

@@ -36,7 +36,7 @@ def test_host_only_calls(repo_root):
     import int8_gemm_amd as g
     lib = g.load()
     assert lib.i8g_version().startswith(b"int8_gemm")
-    for st in range(6):
+    for st in range(7):
         assert lib.i8g_status_string(st)
     assert lib.i8g_status_string(99) == b"unknown status"
     assert g.workspace_bytes(256, 256, 256) >= 256
