@@ -13,6 +13,9 @@ Modules
                  by ``ieee32``.
 ``hashref``      the output-hash definition (numpy uint64 and pure Python).
 ``adversarial``  searches that build tie and near-tie inputs (uses ``ref``).
+``formats``      power-of-two scales and int4 values (two per byte), numpy
+                 and exact-rational versions.
+``probe``        the seeded inputs and hash of the kernel probe.
 
 The method is the block-scaled int8 GEMM of the DaisyChain-Train page
 "Verification — why you can trust the numbers", section "The verified INT8
