@@ -69,6 +69,14 @@ extern "C" {
 /* flags of gemm_i8_blockscaled */
 #define I8G_RELU 1u        /* fused ReLU: out = out > 0 ? out : +0          */
 #define I8G_HASH 2u        /* also write the output hash to *hash            */
+#define I8G_A_INT4 4u      /* QA holds int4 values, two per byte (see below) */
+#define I8G_B_INT4 8u      /* QBt holds int4 values, two per byte            */
+
+/* Storage formats of quantize_rows_fmt / quantize_cols_fmt (the presk page,
+ * section "Integer weights": int8 or int4 values, absmax or power-of-two
+ * scales). */
+#define I8G_FMT_POW2 1u    /* scale rounded up to a power of two: q*s exact  */
+#define I8G_FMT_INT4 2u    /* qmax 7 instead of 127, two values per byte     */
 
 /* Largest K for which |acc| <= 127*127*K stays below 2^31. */
 #define I8G_K_MAX 133144
@@ -105,6 +113,30 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                   int8_t* Qt, int64_t ldqt, float* scale, void* stream);
 
 /*
+ * quantize_rows_fmt / quantize_cols_fmt -- quantize_rows / quantize_cols in
+ * one of the storage formats of the presk page, section "Integer weights"
+ * (b-bit values with qmax = 2^(b-1) - 1; scales absmax or rounded up to a
+ * power of two, "at most twice as coarse" so that q*s is exact; int4 values
+ * two to a byte).  format = 0 is exactly quantize_rows / quantize_cols.
+ *   scale  s = max(RN(a/qmax), RN(1e-8)) with qmax = 127, or 7 with
+ *          I8G_FMT_INT4; with I8G_FMT_POW2, s is then replaced by the
+ *          smallest power of two >= s (so the floor becomes 2^-26).
+ *   values q = floor(RN(RN(x * RN(1/s)) + 0.5)), |q| <= qmax.
+ *   int4 layout (I8G_FMT_INT4): a line of L values (a row of Q, a row of
+ *          Qt) takes 16*ceil(L/32) bytes; value k sits in byte
+ *          16*(k/32) + k%16, in the low nibble when k%32 < 16 and in the
+ *          high nibble otherwise, as a 4-bit two's complement number;
+ *          nibbles past L are written 0.  Q (Qt) must be 16-byte aligned and
+ *          ldq (ldqt) a multiple of 16 of at least 16*ceil(L/32) bytes.
+ * Errors: as quantize_rows / quantize_cols, plus I8G_EINVAL for unknown
+ * format bits and I8G_EALIGN for a misaligned int4 output.
+ */
+int quantize_rows_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                      int8_t* Q, int64_t ldq, float* scale, uint32_t format, void* stream);
+int quantize_cols_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                      int8_t* Qt, int64_t ldqt, float* scale, uint32_t format, void* stream);
+
+/*
  * gemm_i8_blockscaled -- C = epilogue(QA . QBt^T) (steps 2 and 3 of "The
  * verified INT8 units").
  *   QA     M x K int8, row-major (K contiguous), leading dimension lda.
@@ -113,7 +145,10 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
  *          rows, leading dimension ldb.
  *   s_col  N f32 column scales of B.
  *   C      M x N f32 output, row-major, leading dimension ldc >= N.
- *   flags  I8G_RELU and/or I8G_HASH.
+ *   flags  I8G_RELU and/or I8G_HASH; I8G_A_INT4 / I8G_B_INT4 when QA / QBt
+ *          hold int4 values in the layout of quantize_rows_fmt (then that
+ *          operand's ld need only cover 16*ceil(K/32) bytes).  Scales of
+ *          either scheme are taken as they are.
  *   hash   device pointer to one uint64_t, required with I8G_HASH (else
  *          ignored): receives output_hash(C) for this output.
  *   workspace, workspace_bytes

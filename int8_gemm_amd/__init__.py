@@ -10,6 +10,9 @@ entry points have the names of the C ABI in ``include/int8_gemm.h``:
                                      -> C  or  (C, hash_tensor)
     output_hash(C)                   -> hash_tensor     (1 element, device)
     blockscaled_gemm(A, B, relu=False, want_hash=False)  A @ B, all steps
+    quantize_rows_fmt(X, fmt) / quantize_cols_fmt(X, fmt)   FMT_POW2 / FMT_INT4
+                                     storage formats (int4: 16*ceil(len/32) bytes per line)
+    gemm_i8_blockscaled(..., K=K, a_int4=True / b_int4=True)  int4 operands
 
 Hash tensors hold the 64-bit hash in an int64 element; ``hash_value``
 returns it as a Python int in [0, 2^64).  If the library is not built, or
@@ -22,17 +25,22 @@ import torch
 
 __all__ = ["quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "output_hash",
            "blockscaled_gemm", "hash_value", "workspace_bytes", "library_path", "load",
-           "I8G_RELU", "I8G_HASH", "K_MAX", "I8GError"]
+           "I8G_RELU", "I8G_HASH", "K_MAX", "I8GError", "quantize_rows_fmt", "quantize_cols_fmt",
+           "FMT_POW2", "FMT_INT4", "int4_line_bytes"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libint8_gemm.so")
 I8G_RELU = 1
 I8G_HASH = 2
+I8G_A_INT4 = 4
+I8G_B_INT4 = 8
+FMT_POW2 = 1
+FMT_INT4 = 2
 K_MAX = 133144
 EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_workspace_bytes",
             "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version",
             "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
-            "i8g_probe_hash", "i8g_probe_workspace_bytes")
+            "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt")
 
 _lib = None
 _ws = {}
@@ -62,6 +70,10 @@ def load():
     lib.quantize_rows.restype = ctypes.c_int
     lib.quantize_cols.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]
     lib.quantize_cols.restype = ctypes.c_int
+    lib.quantize_rows_fmt.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_u32, c_vp]
+    lib.quantize_rows_fmt.restype = ctypes.c_int
+    lib.quantize_cols_fmt.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_u32, c_vp]
+    lib.quantize_cols_fmt.restype = ctypes.c_int
     lib.gemm_i8_blockscaled.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                                         c_vp, c_i64, c_u32, c_vp, c_vp, c_sz, c_vp]
     lib.gemm_i8_blockscaled.restype = ctypes.c_int
@@ -151,6 +163,42 @@ def quantize_cols(X):
     return Qt, s
 
 
+def int4_line_bytes(n):
+    """Bytes of one int4 line of n values (whole 16-byte groups of 32)."""
+    return 16 * ((n + 31) // 32)
+
+
+def _line_buffer(lines, n, fmt, device):
+    if fmt & FMT_INT4:
+        return torch.empty((lines, max(int4_line_bytes(n), 16)), dtype=torch.int8,
+                           device=device)[:, :int4_line_bytes(n)]
+    return _int8_padded(lines, n, device)
+
+
+def quantize_rows_fmt(X, fmt):
+    """quantize_rows in storage format ``fmt`` (FMT_POW2 | FMT_INT4 bits).
+    int4: Q is rows x int4_line_bytes(cols) int8 (the packed bytes)."""
+    _req_matrix(X, torch.float32, "X")
+    rows, cols = X.shape
+    Q = _line_buffer(rows, cols, fmt, X.device)
+    s = torch.empty(rows, dtype=torch.float32, device=X.device)
+    _check(load().quantize_rows_fmt(_ptr(X), rows, cols, _ld(X), _ptr(Q), Q.stride(0), _ptr(s),
+                                    fmt, _stream(X)))
+    return Q, s
+
+
+def quantize_cols_fmt(X, fmt):
+    """quantize_cols in storage format ``fmt``; int4: Qt is cols x
+    int4_line_bytes(rows)."""
+    _req_matrix(X, torch.float32, "X")
+    rows, cols = X.shape
+    Qt = _line_buffer(cols, rows, fmt, X.device)
+    s = torch.empty(cols, dtype=torch.float32, device=X.device)
+    _check(load().quantize_cols_fmt(_ptr(X), rows, cols, _ld(X), _ptr(Qt), Qt.stride(0), _ptr(s),
+                                    fmt, _stream(X)))
+    return Qt, s
+
+
 def workspace_bytes(M, N, K):
     return int(load().gemm_i8_workspace_bytes(M, N, K))
 
@@ -168,13 +216,20 @@ def _workspace(device, nbytes):
     return ws
 
 
-def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=None):
+def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=None, K=None,
+                        a_int4=False, b_int4=False):
+    """C = epilogue(QA . QBt^T).  With a_int4 / b_int4 the operand holds
+    packed int4 lines (quantize_*_fmt with FMT_INT4) and K must be given."""
     _req_matrix(QA, torch.int8, "QA")
     _req_matrix(QBt, torch.int8, "QBt")
-    M, K = QA.shape
-    N, K2 = QBt.shape
-    if K2 != K:
-        raise ValueError(f"K mismatch: QA has {K}, QBt has {K2}")
+    M, ka = QA.shape
+    N, kb = QBt.shape
+    if K is None:
+        if a_int4 or b_int4:
+            raise ValueError("K is required with int4 operands")
+        K = ka
+    if ka != (int4_line_bytes(K) if a_int4 else K) or kb != (int4_line_bytes(K) if b_int4 else K):
+        raise ValueError(f"operand widths {ka}, {kb} do not match K = {K}")
     if s_row.dtype != torch.float32 or s_col.dtype != torch.float32:
         raise ValueError("scales must be float32")
     if s_row.numel() != M or s_col.numel() != N:
@@ -187,7 +242,8 @@ def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=
     h = torch.zeros(1, dtype=torch.int64, device=dev) if want_hash else None
     nbytes = workspace_bytes(M, N, K)
     ws = _workspace(dev, nbytes)
-    flags = (I8G_RELU if relu else 0) | (I8G_HASH if want_hash else 0)
+    flags = ((I8G_RELU if relu else 0) | (I8G_HASH if want_hash else 0) |
+             (I8G_A_INT4 if a_int4 else 0) | (I8G_B_INT4 if b_int4 else 0))
     lda = QA.stride(0) if M > 0 else _round16(K)
     ldb = QBt.stride(0) if N > 0 else _round16(K)
     _check(load().gemm_i8_blockscaled(

@@ -36,7 +36,8 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
                  hipStream_t stream, int force_tile, int force_splits) {
   if (M < 0 || N < 0 || K < 0) return I8G_EINVAL;
   if (M > INT32_MAX || N > INT32_MAX) return I8G_EINVAL;
-  if (flags & ~(I8G_RELU | I8G_HASH)) return I8G_EINVAL;
+  if (flags & ~(I8G_RELU | I8G_HASH | I8G_A_INT4 | I8G_B_INT4)) return I8G_EINVAL;
+  const bool a4 = (flags & I8G_A_INT4) != 0, b4 = (flags & I8G_B_INT4) != 0;
   const bool want_hash = (flags & I8G_HASH) != 0;
   if (want_hash && !hash) return I8G_EINVAL;
   if (K > I8G_K_MAX) return I8G_EKRANGE;
@@ -48,15 +49,16 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
   }
   if (!C || !s_row || !s_col || ldc < N) return I8G_EINVAL;
   if (K > 0 && (!QA || !QBt)) return I8G_EINVAL;
-  const int64_t k16 = (K + 15) / 16 * 16;
+  const int64_t k16 = (K + 15) / 16 * 16, k4 = (K + 31) / 32 * 16;   // row bytes: int8, int4
   if (K > 0) {
-    if (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < k16 ||
-        ldb < k16)
+    if (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) ||
+        lda < (a4 ? k4 : k16) || ldb < (b4 ? k4 : k16))
       return I8G_EALIGN;
   }
   // force_tile == -2: the library's own choice (plan_gemm, which honours the
   // test overrides); otherwise exactly the forced configuration
-  GemmPlan plan = force_tile == -2
+  GemmPlan plan = (a4 || b4) ? plan_gemm_int4(M, N, K > 0 ? K : 1, force_tile == -2 ? -1 : force_splits)
+                  : force_tile == -2
                       ? plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc)
                       : plan_gemm_forced(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc, force_tile, force_splits);
   if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
@@ -86,6 +88,8 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
   p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
   p.comb_rows = plan.comb_rows;
   p.hash_out = hash;
+  p.a4 = a4 ? 1 : 0;
+  p.b4 = b4 ? 1 : 0;
   return hip_status(launch_gemm(p, plan, stream));
 }
 
@@ -98,7 +102,7 @@ const char* i8g_status_string(int status) {
     case I8G_OK: return "ok";
     case I8G_EINVAL: return "invalid argument (null pointer, negative size or leading dimension too small)";
     case I8G_EKRANGE: return "K exceeds 133144: exact int32 accumulation is not guaranteed";
-    case I8G_EALIGN: return "GEMM operand not 16-byte aligned, or its leading dimension is not a multiple of 16 at least K rounded up to 16";
+    case I8G_EALIGN: return "operand not 16-byte aligned, or its leading dimension not a multiple of 16 covering a whole row (K rounded up to 16 bytes; int4: 16 bytes per 32 values)";
     case I8G_EWORKSPACE: return "workspace missing, misaligned or smaller than gemm_i8_workspace_bytes()";
     case I8G_EHIP: return "HIP runtime error while enqueueing a kernel";
     case I8G_EGATE: return "self-check failed: a device output differs from the exact host mirror";
@@ -108,20 +112,38 @@ const char* i8g_status_string(int status) {
 
 const char* i8g_version(void) { return "int8_gemm 0.1.0 gfx950"; }
 
-int quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
-                  float* scale, void* stream) {
-  int st = check_quantize_args(X, rows, cols, ldx, Q, cols, ldq, scale);
+int quantize_rows_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q,
+                      int64_t ldq, float* scale, uint32_t format, void* stream) {
+  if (format & ~(I8G_FMT_POW2 | I8G_FMT_INT4)) return I8G_EINVAL;
+  const bool int4 = (format & I8G_FMT_INT4) != 0;
+  const int64_t line_bytes = int4 ? (cols + 31) / 32 * 16 : cols;
+  int st = check_quantize_args(X, rows, cols, ldx, Q, line_bytes, ldq, scale);
   if (st != I8G_OK || rows == 0) return st;
   if (cols == 0 && !scale) return I8G_EINVAL;   // empty rows still get the floor scale
-  return hip_status(launch_quantize_rows(X, rows, cols, ldx, Q, ldq, scale, as_stream(stream)));
+  if (int4 && cols > 0 && (((uintptr_t)Q % 16) || (ldq % 16))) return I8G_EALIGN;
+  return hip_status(launch_quantize_rows(X, rows, cols, ldx, Q, ldq, scale, (int)format, as_stream(stream)));
+}
+
+int quantize_cols_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
+                      int64_t ldqt, float* scale, uint32_t format, void* stream) {
+  if (format & ~(I8G_FMT_POW2 | I8G_FMT_INT4)) return I8G_EINVAL;
+  const bool int4 = (format & I8G_FMT_INT4) != 0;
+  const int64_t line_bytes = int4 ? (rows + 31) / 32 * 16 : rows;
+  int st = check_quantize_args(X, rows, cols, ldx, Qt, line_bytes, ldqt, scale);
+  if (st != I8G_OK || cols == 0) return st;
+  if (rows == 0 && !scale) return I8G_EINVAL;   // empty columns still get the floor scale
+  if (int4 && rows > 0 && (((uintptr_t)Qt % 16) || (ldqt % 16))) return I8G_EALIGN;
+  return hip_status(launch_quantize_cols(X, rows, cols, ldx, Qt, ldqt, scale, (int)format, as_stream(stream)));
+}
+
+int quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
+                  float* scale, void* stream) {
+  return quantize_rows_fmt(X, rows, cols, ldx, Q, ldq, scale, 0u, stream);
 }
 
 int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
                   int64_t ldqt, float* scale, void* stream) {
-  int st = check_quantize_args(X, rows, cols, ldx, Qt, rows, ldqt, scale);
-  if (st != I8G_OK || cols == 0) return st;
-  if (rows == 0 && !scale) return I8G_EINVAL;   // empty columns still get the floor scale
-  return hip_status(launch_quantize_cols(X, rows, cols, ldx, Qt, ldqt, scale, as_stream(stream)));
+  return quantize_cols_fmt(X, rows, cols, ldx, Qt, ldqt, scale, 0u, stream);
 }
 
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -130,7 +152,9 @@ size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   // kernel): size for either
   const GemmPlan a = plan_gemm(M, N, K > 0 ? K : 1, true);
   const GemmPlan b = plan_gemm(M, N, K > 0 ? K : 1, false);
+  const GemmPlan c = plan_gemm_int4(M, N, K > 0 ? K : 1, -1);   // int4 operands
   size_t bytes = a.workspace_bytes > b.workspace_bytes ? a.workspace_bytes : b.workspace_bytes;
+  bytes = bytes > c.workspace_bytes ? bytes : c.workspace_bytes;
   return bytes > 256 ? bytes : 256;
 }
 

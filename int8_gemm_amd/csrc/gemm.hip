@@ -450,6 +450,202 @@ gemm_i8_dma_kernel(const GemmParams p) {
   epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, tm, tn, split);
 }
 
+// ---------------------------------------------------------------------------
+// Operands stored as int4 (I8G_A_INT4 / I8G_B_INT4), register-staged: each
+// 16-byte group of packed values (32 values: the low nibbles of its bytes are
+// values 0..15, the high nibbles values 16..31) is widened in registers to
+// two 16-byte int8 chunks and written to the same swizzled LDS layout as the
+// int8 kernels use.  The widening keeps each nibble in the high half of its
+// byte: chunk 0 = (w << 4) & 0xF0F0F0F0, chunk 1 = w & 0xF0F0F0F0, i.e. the
+// int8 value 16*q, exact for q in [-8, 7].  The MFMAs then sum
+// 16^(a4+b4) * qa * qb exactly (|16*7*127| and |16*7*16*7| are below 127^2,
+// so the int32 range of the K limit still holds) and the accumulators are
+// shifted right by 4*(a4+b4) before the epilogue, which is exact because
+// every term is a multiple of that power of two.  Two LDS buffers, one
+// barrier per 64-value stage, the next stage's global loads in flight during
+// the current stage's MFMAs.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A4, bool B4>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
+gemm_i4_kernel(const GemmParams p) {
+  constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  constexpr int A_PER_ROW = A4 ? 2 : 4, B_PER_ROW = B4 ? 2 : 4;   // 16-byte loads per row per stage
+  constexpr int A_LD = BM * A_PER_ROW / NT, B_LD = BN * B_PER_ROW / NT;
+  static_assert(A_LD * NT == BM * A_PER_ROW && B_LD * NT == BN * B_PER_ROW, "loads per thread");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[dma_smem_bytes<BM, BN, WAVES_M, WAVES_N, 2>()];
+  int tm, tn, split;
+  map_workgroup(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.splits, tm, tn, split);
+  const int k_begin = split * p.k_per_split;
+  int k_end = k_begin + p.k_per_split;
+  if (k_end > p.K) k_end = p.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // this thread's loads: (row, 16-byte position within the stage's row)
+  const int8_t* pa[A_LD];
+  const int8_t* pb[B_LD];
+  int ra_row[A_LD], ra_pos[A_LD], rb_row[B_LD], rb_pos[B_LD];
+#pragma unroll
+  for (int q = 0; q < A_LD; ++q) {
+    const int c = tid + q * NT;
+    ra_row[q] = c / A_PER_ROW;
+    ra_pos[q] = c % A_PER_ROW;
+    int gr = m0 + ra_row[q];
+    gr = gr < p.M ? gr : p.M - 1;
+    pa[q] = p.A + (int64_t)gr * p.lda;
+  }
+#pragma unroll
+  for (int q = 0; q < B_LD; ++q) {
+    const int c = tid + q * NT;
+    rb_row[q] = c / B_PER_ROW;
+    rb_pos[q] = c % B_PER_ROW;
+    int gr = n0 + rb_row[q];
+    gr = gr < p.N ? gr : p.N - 1;
+    pb[q] = p.B + (int64_t)gr * p.ldb;
+  }
+  v4i ga[A_LD], gb[B_LD];
+  const v4i zero = {0, 0, 0, 0};
+  // global -> registers for the stage starting at value k0 (k0 % 64 == 0).
+  // int8: 16 values at k0 + 16*pos; int4: 32 values at k0 + 32*pos, i.e. 16
+  // bytes at byte (k0 + 32*pos) / 2, which lies inside the row whenever its
+  // first value does (a row holds whole 16-byte groups).
+  auto gload = [&](int k0) {
+    const bool full = k0 + BK <= k_end;
+#pragma unroll
+    for (int q = 0; q < A_LD; ++q) {
+      if (A4) {
+        const int kk = k0 + 32 * ra_pos[q];
+        ga[q] = (full || kk < k_end) ? *reinterpret_cast<const v4i*>(pa[q] + kk / 2) : zero;
+      } else {
+        const int kk = k0 + 16 * ra_pos[q];
+        ga[q] = full ? *reinterpret_cast<const v4i*>(pa[q] + kk) : load_chunk(pa[q], kk, k_end);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < B_LD; ++q) {
+      if (B4) {
+        const int kk = k0 + 32 * rb_pos[q];
+        gb[q] = (full || kk < k_end) ? *reinterpret_cast<const v4i*>(pb[q] + kk / 2) : zero;
+      } else {
+        const int kk = k0 + 16 * rb_pos[q];
+        gb[q] = full ? *reinterpret_cast<const v4i*>(pb[q] + kk) : load_chunk(pb[q], kk, k_end);
+      }
+    }
+  };
+  auto widen_lo = [](v4i w) {
+    v4i r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (int)(((unsigned int)w[e] << 4) & 0xF0F0F0F0u);
+    return r;
+  };
+  auto widen_hi = [](v4i w) {
+    v4i r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (int)((unsigned int)w[e] & 0xF0F0F0F0u);
+    return r;
+  };
+  // registers -> LDS buffer `buf` (int4 widened; values >= k_end zeroed)
+  auto sstore = [&](int buf, int k0) {
+    const bool full = k0 + BK <= k_end;
+    int8_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int q = 0; q < A_LD; ++q) {
+      int8_t* rowp = base + ra_row[q] * BK;
+      if (A4) {
+        const int kk = k0 + 32 * ra_pos[q];
+        v4i lo = widen_lo(ga[q]), hi = widen_hi(ga[q]);
+        if (!full) {
+          lo = mask_tail(lo, k_end - kk);
+          hi = mask_tail(hi, k_end - kk - 16);
+        }
+        *reinterpret_cast<v4i*>(rowp + (swz(ra_row[q], 2 * ra_pos[q]) << 4)) = lo;
+        *reinterpret_cast<v4i*>(rowp + (swz(ra_row[q], 2 * ra_pos[q] + 1) << 4)) = hi;
+      } else {
+        *reinterpret_cast<v4i*>(rowp + (swz(ra_row[q], ra_pos[q]) << 4)) = ga[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < B_LD; ++q) {
+      int8_t* rowp = base + A_BYTES + rb_row[q] * BK;
+      if (B4) {
+        const int kk = k0 + 32 * rb_pos[q];
+        v4i lo = widen_lo(gb[q]), hi = widen_hi(gb[q]);
+        if (!full) {
+          lo = mask_tail(lo, k_end - kk);
+          hi = mask_tail(hi, k_end - kk - 16);
+        }
+        *reinterpret_cast<v4i*>(rowp + (swz(rb_row[q], 2 * rb_pos[q]) << 4)) = lo;
+        *reinterpret_cast<v4i*>(rowp + (swz(rb_row[q], 2 * rb_pos[q] + 1) << 4)) = hi;
+      } else {
+        *reinterpret_cast<v4i*>(rowp + (swz(rb_row[q], rb_pos[q]) << 4)) = gb[q];
+      }
+    }
+  };
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  int offa[2][FM], offb[2][FN];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * WTM + i * 32 + lrow;
+      offa[s][i] = row * BK + (swz(row, s * 2 + lhalf) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WTN + j * 32 + lrow;
+      offb[s][j] = A_BYTES + row * BK + (swz(row, s * 2 + lhalf) << 4);
+    }
+  }
+  const int klen = k_end > k_begin ? k_end - k_begin : 0;
+  const int nst = (klen + BK - 1) / BK;
+  if (nst > 0) gload(k_begin);
+  for (int kt = 0; kt < nst; ++kt) {
+    const int buf = kt & 1;
+    // buffer `buf` was last read in stage kt-2; every wave has passed the
+    // barrier of stage kt-1 since, so it is free
+    sstore(buf, k_begin + kt * BK);
+    __syncthreads();
+    if (kt + 1 < nst) gload(k_begin + (kt + 1) * BK);
+    const int8_t* sb = smem + buf * STAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      v4i fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const v4i*>(sb + offa[s][i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const v4i*>(sb + offb[s][j]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();   // the epilogue reuses the LDS
+  constexpr int SHIFT = 4 * ((A4 ? 1 : 0) + (B4 ? 1 : 0));
+  if (SHIFT > 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] >>= SHIFT;
+  }
+  epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, tm, tn, split);
+}
+
 // Calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -1650,6 +1846,15 @@ static int env_int(const char* name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
+constexpr int kCfgInt4 = kNumCfgs;   // gemm_i4_kernel, planned as the 128x128 tile
+
+GemmPlan plan_gemm_int4(int64_t M, int64_t N, int64_t K, int force_splits) {
+  GemmPlan plan = plan_gemm_forced(M, N, K, false, 2,
+                                   force_splits < 0 ? env_int("I8G_FORCE_SPLITS", 0) : force_splits);
+  if (plan.bm != 0) plan.cfg = kCfgInt4;
+  return plan;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
   return plan_gemm_forced(M, N, K, allow_persistent, env_int("I8G_FORCE_TILE", -1),
                           env_int("I8G_FORCE_SPLITS", 0));
@@ -1776,6 +1981,14 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
         hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, true>), dim3(grid), dim3(256), 0, stream, p);
       else
         hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+    case kCfgInt4:
+      if (p.a4 && p.b4)
+        hipLaunchKernelGGL((gemm_i4_kernel<128, 128, 2, 2, true, true>), dim3(grid), dim3(256), 0, stream, p);
+      else if (p.a4)
+        hipLaunchKernelGGL((gemm_i4_kernel<128, 128, 2, 2, true, false>), dim3(grid), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_i4_kernel<128, 128, 2, 2, false, true>), dim3(grid), dim3(256), 0, stream, p);
       break;
     default:
       if (p.relu)

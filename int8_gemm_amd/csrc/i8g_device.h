@@ -46,6 +46,30 @@ __device__ __forceinline__ float scale_of_absmax(float a) {
 
 __device__ __forceinline__ float recip_rn(float s) { return div_rn(1.0f, s); }
 
+// Storage formats of the quantize passes (the presk page, section "Integer
+// weights": int8 or int4 values, absmax or power-of-two scales).
+constexpr int FMT_POW2 = 1;   // the scale rounded up to a power of two
+constexpr int FMT_INT4 = 2;   // values in [-7, 7] (qmax = 2^(4-1) - 1), two per byte
+
+// Smallest power of two >= s for a positive normal s (the exponent field
+// cannot overflow: s <= FLT_MAX / 7 < 2^126).
+__device__ __forceinline__ float pow2_ceil(float s) {
+  uint32_t b = __float_as_uint(s);
+  if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
+  return __uint_as_float(b);
+}
+
+// s = max(RN(a/qmax), RN(1e-8)), then rounded up to a power of two for
+// FMT_POW2; qmax = 127 for int8, 7 for int4.
+template <int FMT>
+__device__ __forceinline__ float scale_of_absmax_fmt(float a) {
+  float s = div_rn(a, (FMT & FMT_INT4) ? 7.0f : 127.0f);
+  const float f = scale_floor();
+  s = s > f ? s : f;
+  if (FMT & FMT_POW2) s = pow2_ceil(s);
+  return s;
+}
+
 // q = floor(RN(RN(x*inv) + 0.5)), in [-127, 127] for |x| <= the line max.
 __device__ __forceinline__ int quantize1(float x, float inv) {
   float t = mul_rn(x, inv);

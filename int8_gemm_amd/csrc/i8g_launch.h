@@ -24,6 +24,7 @@ struct GemmParams {
   int* partials;                    // split-K int32 partial sums, [split][M][N]
   int comb_rows;                    // rows per split-K combine workgroup
   uint64_t* hash_out;
+  int a4, b4;                       // operand stored as int4, two per byte (gemm_i4_kernel only)
 };
 
 struct GemmPlan {
@@ -58,12 +59,18 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
                  const float* s_col, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
                  uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,
                  hipStream_t stream, int force_tile, int force_splits);
+// Plan for int4 operands: the register-staged kernel, 128x128 tiles, split
+// K as the cost model of that tile chooses (force_splits as above; < 0 reads
+// I8G_FORCE_SPLITS).
+GemmPlan plan_gemm_int4(int64_t M, int64_t N, int64_t K, int force_splits);
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
 
+// fmt: FMT_POW2 / FMT_INT4 bits (i8g_device.h); int4 outputs take
+// 16*ceil(len/32) bytes per line, 16-byte aligned.
 hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,
-                                int8_t* Q, int64_t ldq, float* scale, hipStream_t stream);
+                                int8_t* Q, int64_t ldq, float* scale, int fmt, hipStream_t stream);
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
-                                int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream);
+                                int8_t* Qt, int64_t ldqt, float* scale, int fmt, hipStream_t stream);
 hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
                               uint64_t* hash, void* workspace, hipStream_t stream);
 

@@ -65,7 +65,7 @@ __device__ __forceinline__ void store4(int8_t* row, int64_t c, int64_t cols, uns
 // ---------------------------------------------------------------------------
 // rows: one wavefront per row, VPL groups of 4 elements per lane in registers
 // ---------------------------------------------------------------------------
-template <int VPL>
+template <int VPL, int FMT>
 __global__ void __launch_bounds__(256)
 qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
                   int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
@@ -82,7 +82,7 @@ qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
     m = absmax4(m, v[i]);
   }
   m = wave_max_f32(m);
-  const float s = scale_of_absmax(m);
+  const float s = scale_of_absmax_fmt<FMT>(m);
   const float inv = recip_rn(s);
   if (lane == 0) scale[r] = s;
   int8_t* qr = Q + r * ldq;
@@ -96,7 +96,7 @@ qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
 // ---------------------------------------------------------------------------
 // rows: one 1024-thread workgroup per row (long rows)
 // ---------------------------------------------------------------------------
-template <int VPT>
+template <int VPT, int FMT>
 __global__ void __launch_bounds__(1024)
 qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
                    int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
@@ -126,7 +126,7 @@ qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
     if (lane == 0) red[0] = w;
   }
   __syncthreads();
-  const float s = scale_of_absmax(red[0]);
+  const float s = scale_of_absmax_fmt<FMT>(red[0]);
   const float inv = recip_rn(s);
   if (tid == 0) scale[r] = s;
   if (cols <= CHUNK) {   // the row is still in registers
@@ -146,32 +146,33 @@ qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
   }
 }
 
-hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,
-                                int8_t* Q, int64_t ldq, float* scale, hipStream_t stream) {
+template <int FMT>
+hipError_t quantize_rows_int8(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                              int8_t* Q, int64_t ldq, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
   if (cols <= 256 * 16) {
     const dim3 grid((unsigned int)((rows + 3) / 4)), block(256);
     if (cols <= 256)
-      hipLaunchKernelGGL(qrows_wave_kernel<1>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<1, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 512)
-      hipLaunchKernelGGL(qrows_wave_kernel<2>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<2, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 768)
-      hipLaunchKernelGGL(qrows_wave_kernel<3>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<3, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 1024)
-      hipLaunchKernelGGL(qrows_wave_kernel<4>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<4, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 2048)
-      hipLaunchKernelGGL(qrows_wave_kernel<8>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<8, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 3072)
-      hipLaunchKernelGGL(qrows_wave_kernel<12>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<12, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else
-      hipLaunchKernelGGL(qrows_wave_kernel<16>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_wave_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
   } else {
     const dim3 grid((unsigned int)rows), block(1024);
     if (cols <= 1024 * 8 * 4)
-      hipLaunchKernelGGL(qrows_block_kernel<8>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_block_kernel<8, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else
-      hipLaunchKernelGGL(qrows_block_kernel<16>, grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      hipLaunchKernelGGL((qrows_block_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
   }
   return hipGetLastError();
 }
@@ -189,14 +190,16 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
 //     cache), quantizes 64x64 tiles with inv = RN(1/s), transposes them
 //     through LDS and writes K-contiguous rows of Qt.
 // ---------------------------------------------------------------------------
+template <int FMT>
 __global__ void qcols_init_kernel(float* scale, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) scale[i] = scale_floor();
+  if (i < n) scale[i] = scale_of_absmax_fmt<FMT>(0.0f);   // the (rounded) floor
 }
 
 constexpr int QS_ROWS = 64;     // rows per workgroup of qcols_scale_kernel
 constexpr int QS_COLS = 256;    // columns per workgroup (64 lanes x 4)
 
+template <int FMT>
 __global__ void __launch_bounds__(256)
 qcols_scale_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
                    float* __restrict__ scale, int vec_in) {
@@ -236,7 +239,7 @@ qcols_scale_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
   const float a = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
   const int64_t col = (int64_t)blockIdx.x * QS_COLS + tid;
   if (col < cols)
-    atomicMax(reinterpret_cast<unsigned int*>(scale) + col, __float_as_uint(scale_of_absmax(a)));
+    atomicMax(reinterpret_cast<unsigned int*>(scale) + col, __float_as_uint(scale_of_absmax_fmt<FMT>(a)));
 }
 
 // Quantize a 64 (rows of X = k) x 64 (columns of X = j) tile with the column
@@ -314,7 +317,7 @@ __device__ __forceinline__ int xcd_grouped(int wg, int total) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
-template <int BC>
+template <int BC, int FMT>
 __global__ void __launch_bounds__(QCR_THREADS)
 qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
                  int8_t* __restrict__ Qt, int64_t ldqt, float* __restrict__ scale, int vec_in,
@@ -360,7 +363,7 @@ qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_
     float a = 0.f;
 #pragma unroll
     for (int w = 0; w < QCR_THREADS / 64; ++w) a = fmaxf(a, red[w][tid]);
-    const float s = scale_of_absmax(a);
+    const float s = scale_of_absmax_fmt<FMT>(a);
     s_inv[tid] = recip_rn(s);
     if (j0 + tid < cols) scale[j0 + tid] = s;
   }
@@ -407,8 +410,9 @@ static int qcols_band(int64_t rows, int64_t cols) {
   return bc;
 }
 
-hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
-                                int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream) {
+template <int FMT>
+hipError_t quantize_cols_int8(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                              int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Qt % 16 == 0) && (ldqt % 16 == 0);
   int bc = rows > 0 ? qcols_band(rows, cols) : 0;
@@ -419,18 +423,18 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
   if (bc > 0) {
     const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
     switch (bc) {
-      case 64: hipLaunchKernelGGL(qcols_reg_kernel<64>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
-      case 32: hipLaunchKernelGGL(qcols_reg_kernel<32>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
-      case 16: hipLaunchKernelGGL(qcols_reg_kernel<16>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
-      case 8: hipLaunchKernelGGL(qcols_reg_kernel<8>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
-      default: hipLaunchKernelGGL(qcols_reg_kernel<4>, grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 64: hipLaunchKernelGGL((qcols_reg_kernel<64, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 32: hipLaunchKernelGGL((qcols_reg_kernel<32, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 16: hipLaunchKernelGGL((qcols_reg_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      case 8: hipLaunchKernelGGL((qcols_reg_kernel<8, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
+      default: hipLaunchKernelGGL((qcols_reg_kernel<4, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out); break;
     }
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(qcols_init_kernel, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(qcols_init_kernel<FMT>, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
                      stream, scale, cols);
   if (rows > 0) {
-    hipLaunchKernelGGL(qcols_scale_kernel,
+    hipLaunchKernelGGL(qcols_scale_kernel<FMT>,
                        dim3((unsigned int)((cols + QS_COLS - 1) / QS_COLS),
                             (unsigned int)((rows + QS_ROWS - 1) / QS_ROWS)),
                        dim3(256), 0, stream, X, rows, cols, ldx, scale, vec_in);
@@ -439,6 +443,130 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
                        dim3(256), 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out);
   }
   return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// int4 storage (FMT_INT4): values in [-7, 7], two per byte.  Element k of a
+// line sits in byte 16*(k/32) + k%16 of the line, in the low nibble when
+// k%32 < 16 and in the high nibble otherwise (4-bit two's complement); a line
+// of length L takes 16*ceil(L/32) bytes, nibbles past L are 0.  The order
+// lets the GEMM widen a 16-byte group to two int8 chunks with one AND each.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 pack_int4_group(const int (&q)[32]) {
+  unsigned int w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned int v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const unsigned int lo = (unsigned int)q[4 * i + b] & 0xFu;
+      const unsigned int hi = (unsigned int)q[16 + 4 * i + b] & 0xFu;
+      v |= (lo | (hi << 4)) << (8 * b);
+    }
+    w[i] = v;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Rows to int4: one wavefront per row; the absmax pass reads the row with
+// coalesced loads, the pack pass gives each lane whole 32-element groups
+// (a second read, mostly from cache).
+template <int FMT>
+__global__ void __launch_bounds__(256)
+q4rows_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+              int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* xr = X + r * ldx;
+  float m = 0.0f;
+  for (int64_t c = (int64_t)lane * 4; c < cols; c += 256) m = absmax4(m, load4(xr, c, cols, vec_in));
+  m = wave_max_f32(m);
+  const float s = scale_of_absmax_fmt<FMT>(m);
+  const float inv = recip_rn(s);
+  if (lane == 0) scale[r] = s;
+  const int64_t groups = (cols + 31) / 32;
+  for (int64_t g = lane; g < groups; g += 64) {
+    int q[32];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float4 v = load4(xr, g * 32 + t * 4, cols, vec_in);   // zero past cols -> code 0
+      q[4 * t + 0] = quantize1(v.x, inv);
+      q[4 * t + 1] = quantize1(v.y, inv);
+      q[4 * t + 2] = quantize1(v.z, inv);
+      q[4 * t + 3] = quantize1(v.w, inv);
+    }
+    *reinterpret_cast<uint4*>(Q + r * ldq + g * 16) = pack_int4_group(q);
+  }
+}
+
+// Columns to int4 (after the column scales are final): thread (column j,
+// group g) reads its 32 rows (lanes take consecutive columns, so each row
+// read is coalesced) and writes the 16 bytes of group g of row j of Qt.
+template <int FMT>
+__global__ void __launch_bounds__(256)
+q4cols_pack_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                   int8_t* __restrict__ Qt, int64_t ldqt, const float* __restrict__ scale) {
+  const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t g = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t groups = (rows + 31) / 32;
+  if (j >= cols || g >= groups) return;
+  const float inv = recip_rn(scale[j]);
+  int q[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int64_t k = g * 32 + t;
+    q[t] = quantize1(k < rows ? X[k * ldx + j] : 0.0f, inv);
+  }
+  *reinterpret_cast<uint4*>(Qt + j * ldqt + g * 16) = pack_int4_group(q);
+}
+
+template <int FMT>
+hipError_t quantize_rows_int4(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q,
+                              int64_t ldq, float* scale, hipStream_t stream) {
+  const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
+  hipLaunchKernelGGL(q4rows_kernel<FMT>, dim3((unsigned int)((rows + 3) / 4)), dim3(256), 0, stream, X,
+                     rows, cols, ldx, Q, ldq, scale, vec_in);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t quantize_cols_int4(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
+                              int64_t ldqt, float* scale, hipStream_t stream) {
+  const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
+  hipLaunchKernelGGL(qcols_init_kernel<FMT>, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
+                     stream, scale, cols);
+  if (rows > 0) {
+    hipLaunchKernelGGL(qcols_scale_kernel<FMT>,
+                       dim3((unsigned int)((cols + QS_COLS - 1) / QS_COLS),
+                            (unsigned int)((rows + QS_ROWS - 1) / QS_ROWS)),
+                       dim3(256), 0, stream, X, rows, cols, ldx, scale, vec_in);
+    hipLaunchKernelGGL(q4cols_pack_kernel<FMT>,
+                       dim3((unsigned int)((cols + 63) / 64), (unsigned int)(((rows + 31) / 32 + 3) / 4)),
+                       dim3(256), 0, stream, X, rows, cols, ldx, Qt, ldqt, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q,
+                                int64_t ldq, float* scale, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case 0: return quantize_rows_int8<0>(X, rows, cols, ldx, Q, ldq, scale, stream);
+    case FMT_POW2: return quantize_rows_int8<FMT_POW2>(X, rows, cols, ldx, Q, ldq, scale, stream);
+    case FMT_INT4: return quantize_rows_int4<FMT_INT4>(X, rows, cols, ldx, Q, ldq, scale, stream);
+    default: return quantize_rows_int4<FMT_INT4 | FMT_POW2>(X, rows, cols, ldx, Q, ldq, scale, stream);
+  }
+}
+
+hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
+                                int64_t ldqt, float* scale, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case 0: return quantize_cols_int8<0>(X, rows, cols, ldx, Qt, ldqt, scale, stream);
+    case FMT_POW2: return quantize_cols_int8<FMT_POW2>(X, rows, cols, ldx, Qt, ldqt, scale, stream);
+    case FMT_INT4: return quantize_cols_int4<FMT_INT4>(X, rows, cols, ldx, Qt, ldqt, scale, stream);
+    default: return quantize_cols_int4<FMT_INT4 | FMT_POW2>(X, rows, cols, ldx, Qt, ldqt, scale, stream);
+  }
 }
 
 }  // namespace i8g
