@@ -2,6 +2,7 @@
 """Throughput of the bit-exact block-scaled int8 GEMM path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload mlp|head|step|w1]
+                    [--b-format int8|pow2|int4|int4-pow2]
 
 One step is one pass of the whole path over one batch: per GEMM, the
 quantize pass of each operand (per row, or per column with the transposed
@@ -18,6 +19,8 @@ launched call by call); `roofline` for the step's dominant kernel, whose
 device duration is timed with HIP events around a batch of back-to-back
 launches of that call; `cpu_baseline` = the CPU oracle timed on this host;
 `parity` = whether the oracle's output hashes equal the GPU's.
+--b-format stores every B operand in one of the presk page's "Integer
+weights" formats (the headline line uses the default int8 / absmax).
 """
 import argparse
 import hashlib
@@ -97,8 +100,17 @@ def gemm_mnk(shapes, a_src, a_mode, b_src, b_mode):
 # ---------------------------------------------------------------------------
 # GPU step with preallocated buffers and direct C-ABI calls
 # ---------------------------------------------------------------------------
+# storage formats of the B operands (presk page, "Integer weights"): flag bits
+# of quantize_*_fmt (1 = power-of-two scales, 2 = int4 values two per byte)
+B_FORMATS = {"int8": 0, "pow2": 1, "int4": 2, "int4-pow2": 3}
+
+
+def int4_line_bytes(n):
+    return 16 * ((n + 31) // 32)
+
+
 class GpuStep:
-    def __init__(self, g, torch, tensors, gemms):
+    def __init__(self, g, torch, tensors, gemms, fmt_b=0):
         self.g, self.torch, self.lib = g, torch, g.load()
         dev = torch.device("cuda:0")
         self.dev = dev
@@ -106,17 +118,19 @@ class GpuStep:
         self.sp = self.stream.cuda_stream
         self.t = {k: torch.from_numpy(v).to(dev) for k, v in tensors.items()}
         self.gemms = []
+        self.fmt_b = fmt_b
         ws_bytes = 256
         shapes = {k: tuple(v.shape) for k, v in tensors.items()}
         for (name, a_src, a_mode, b_src, b_mode, relu, out_name) in gemms:
             M, N, K = gemm_mnk(shapes, a_src, a_mode, b_src, b_mode)
             shapes[out_name or name] = (M, N)
             ld = (K + 15) // 16 * 16
-            e = dict(name=name, M=M, N=N, K=K, relu=relu, a_mode=a_mode, a_key=a_src,
+            ldb = int4_line_bytes(K) if fmt_b & 2 else ld
+            e = dict(name=name, M=M, N=N, K=K, relu=relu, a_mode=a_mode, a_key=a_src, ldb=ldb,
                      b_mode=b_mode, b_key=b_src, out=out_name or name,
                      QA=torch.empty((M, ld), dtype=torch.int8, device=dev),
                      sA=torch.empty(M, dtype=torch.float32, device=dev),
-                     QB=torch.empty((N, ld), dtype=torch.int8, device=dev),
+                     QB=torch.empty((N, ldb), dtype=torch.int8, device=dev),
                      sB=torch.empty(N, dtype=torch.float32, device=dev),
                      C=torch.empty((M, N), dtype=torch.float32, device=dev),
                      h=torch.zeros(1, dtype=torch.int64, device=dev), ld=ld)
@@ -125,17 +139,17 @@ class GpuStep:
             self.gemms.append(e)
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
 
-    def _q(self, mode, X, Q, s, ld):
+    def _q(self, mode, X, Q, s, ld, fmt=0):
         rows, cols = X.shape
-        fn = self.lib.quantize_rows if mode == "rows" else self.lib.quantize_cols
-        rc = fn(X.data_ptr(), rows, cols, X.stride(0), Q.data_ptr(), ld, s.data_ptr(), self.sp)
+        fn = self.lib.quantize_rows_fmt if mode == "rows" else self.lib.quantize_cols_fmt
+        rc = fn(X.data_ptr(), rows, cols, X.stride(0), Q.data_ptr(), ld, s.data_ptr(), fmt, self.sp)
         if rc:
             raise RuntimeError(self.lib.i8g_status_string(rc).decode())
 
     def _gemm(self, e):
-        flags = (1 if e["relu"] else 0) | 2
+        flags = (1 if e["relu"] else 0) | 2 | (8 if self.fmt_b & 2 else 0)
         rc = self.lib.gemm_i8_blockscaled(e["QA"].data_ptr(), e["ld"], e["sA"].data_ptr(),
-                                          e["QB"].data_ptr(), e["ld"], e["sB"].data_ptr(),
+                                          e["QB"].data_ptr(), e["ldb"], e["sB"].data_ptr(),
                                           e["M"], e["N"], e["K"], e["C"].data_ptr(), e["N"], flags,
                                           e["h"].data_ptr(), self.ws.data_ptr(), self.ws.numel(),
                                           self.sp)
@@ -145,7 +159,8 @@ class GpuStep:
     def calls(self, e):
         """The three calls of one GEMM of the step, as (label, function)."""
         return (("quantize_A", lambda: self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])),
-                ("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ld"])),
+                ("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ldb"],
+                                               self.fmt_b)),
                 ("gemm", lambda: self._gemm(e)))
 
     def run(self):
@@ -164,10 +179,10 @@ class GpuStep:
 # ---------------------------------------------------------------------------
 # CPU oracle step (the cpu_baseline leg)
 # ---------------------------------------------------------------------------
-def oracle_step(tensors, gemms, budget_s=None):
+def oracle_step(tensors, gemms, budget_s=None, fmt_b=0):
     """The CPU oracle over the GEMMs in order; with a time budget it stops
     after the GEMM that crosses it.  Returns (hashes, int8 ops done)."""
-    from oracle import hashref, ref
+    from oracle import formats, hashref, ref
     t = dict(tensors)
     shapes = {k: tuple(v.shape) for k, v in t.items()}
     hashes, ops = [], 0.0
@@ -176,7 +191,11 @@ def oracle_step(tensors, gemms, budget_s=None):
         M, N, K = gemm_mnk(shapes, a_src, a_mode, b_src, b_mode)
         q = {"rows": ref.quantize_rows, "cols": ref.quantize_cols}
         QA, sA = q[a_mode](t[a_src])
-        QB, sB = q["cols" if b_mode == "cols" else "rows"](t[b_src])
+        if fmt_b:
+            qf = formats.quantize_cols if b_mode == "cols" else formats.quantize_rows
+            QB, sB = qf(t[b_src], fmt_b)
+        else:
+            QB, sB = q["cols" if b_mode == "cols" else "rows"](t[b_src])
         C = ref.gemm_i8_blockscaled(QA, sA, QB, sB, relu)
         t[out_name or name] = C
         shapes[out_name or name] = C.shape
@@ -188,7 +207,7 @@ def oracle_step(tensors, gemms, budget_s=None):
     return hashes, ops
 
 
-def cpu_baseline(tensors, gemms, ops, budget_s=10.0):
+def cpu_baseline(tensors, gemms, ops, budget_s=10.0, fmt_b=0):
     """The oracle timed on this host: whole steps (one to three, about
     budget_s of work) when a step is short, else the leading GEMMs of one
     step up to the budget.  Returns (record, oracle hashes of the GEMMs it ran)."""
@@ -196,7 +215,7 @@ def cpu_baseline(tensors, gemms, ops, budget_s=10.0):
     blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
     threads = max([d.get("num_threads", 1) for d in blas] or [1])
     t0 = time.perf_counter()
-    hashes, done = oracle_step(tensors, gemms, budget_s)
+    hashes, done = oracle_step(tensors, gemms, budget_s, fmt_b)
     first = time.perf_counter() - t0
     if len(hashes) < len(gemms):
         return {"value": done / first / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
@@ -207,7 +226,7 @@ def cpu_baseline(tensors, gemms, ops, budget_s=10.0):
     times = [first]
     while time.perf_counter() - t0 < budget_s and len(times) < 3:
         t1 = time.perf_counter()
-        oracle_step(tensors, gemms)
+        oracle_step(tensors, gemms, None, fmt_b)
         times.append(time.perf_counter() - t1)
     sec = statistics.median(times)
     return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
@@ -250,6 +269,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "step", "w1"])
+    ap.add_argument("--b-format", default="int8", choices=list(B_FORMATS),
+                    help="storage format of every B operand (int4: two values per byte; "
+                         "pow2: power-of-two scales); A operands stay int8 with absmax scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the step captured in a HIP graph")
@@ -269,7 +291,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"[bench] workload {a.workload}: generating inputs")
     desc, tensors, gemms = make_workload(a.workload)
-    step = GpuStep(g, torch, tensors, gemms)
+    fmt_b = B_FORMATS[a.b_format]
+    step = GpuStep(g, torch, tensors, gemms, fmt_b)
     if a.copy_probe > 0:
         src = torch.ones(a.copy_probe << 18, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -359,7 +382,8 @@ def main():
         M, N, K = e["M"], e["N"], e["K"]
         if label == "gemm":
             gops = 2.0 * M * N * K
-            nbytes = M * K + N * K + 4 * M + 4 * N + 4 * M * N + 8
+            b_bytes = N * int4_line_bytes(K) if fmt_b & 2 else N * K
+            nbytes = M * K + b_bytes + 4 * M + 4 * N + 4 * M * N + 8
             bound = "mfma" if gops / nbytes >= RIDGE else "hbm"
             shape = f"{M}x{N}x{K}"
         else:
@@ -367,7 +391,9 @@ def main():
             mode = e["a_mode"] if label == "quantize_A" else e["b_mode"]
             rows, cols = step.t[e["a_key"] if label == "quantize_A" else e["b_key"]].shape
             nscale = rows if mode == "rows" else cols
-            gops, nbytes, bound = 0.0, 5 * rows * cols + 4 * nscale, "hbm"
+            nlines, length = (rows, cols) if mode == "rows" else (cols, rows)
+            qbytes = nlines * int4_line_bytes(length) if (label == "quantize_B" and fmt_b & 2) else rows * cols
+            gops, nbytes, bound = 0.0, 4 * rows * cols + qbytes + 4 * nscale, "hbm"
             shape = f"{rows}x{cols} ({mode})"
         if bound == "mfma":
             ach, peak, unit = gops / (avg * 1e-6) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
@@ -388,7 +414,7 @@ def main():
     parity = None
     if not a.no_cpu_baseline:
         log("[bench] cpu_baseline: oracle on the host")
-        cpu, cpu_hashes = cpu_baseline(tensors, gemms, ops)
+        cpu, cpu_hashes = cpu_baseline(tensors, gemms, ops, fmt_b=fmt_b)
         parity = cpu_hashes == gpu_hashes[:len(cpu_hashes)]
         log(f"[bench] oracle {cpu['value']:.4f} TOPS, parity {parity}")
 
@@ -405,7 +431,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": desc, "name": a.workload,
+        "config": {"workload": desc, "name": a.workload, "b_format": a.b_format,
                    "gemms": [f"{e['M']}x{e['N']}x{e['K']}{' relu' if e['relu'] else ''}"
                              for e in step.gemms],
                    "int8_ops_per_step": ops, "batch": 8, "seq_len": 1024, "tokens": 8192},
