@@ -16,6 +16,7 @@ Modules
 ``formats``      power-of-two scales and int4 values (two per byte), numpy
                  and exact-rational versions.
 ``probe``        the seeded inputs and hash of the kernel probe.
+``requant``      the requantizing epilogue (int8 codes and row scales of the output).
 
 The method is the block-scaled int8 GEMM of the DaisyChain-Train page
 "Verification — why you can trust the numbers", section "The verified INT8
