@@ -178,6 +178,37 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row,
 /* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256). */
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/*
+ * gemm_i8_requant -- the requantizing epilogue: the GEMM's output leaves as
+ * int8 codes and per-row scales, ready to be the A operand of the next GEMM
+ * (the presk page, section "What is left open": activations quantized with
+ * int32 accumulation and requantization; the DaisyChain-Train page, section
+ * "Layer 1: exact init gates", gates such a back-to-back chain).
+ *   QA, lda, s_row, QBt, ldb, s_col, M, N, K   as gemm_i8_blockscaled.
+ *   Q      M x N int8 output, row-major, leading dimension ldq >= N.
+ *   s_out  M f32 output scales.
+ *   flags  I8G_RELU and/or I8G_HASH (hash = output_hash of the f32 output
+ *          y, which is never stored).
+ *   workspace  at least gemm_i8_requant_workspace_bytes(M, N, K) bytes,
+ *          256-byte aligned, first 256 bytes zero as for gemm_i8_blockscaled.
+ * Q and s_out equal quantize_rows(y) byte for byte, y being the output
+ * gemm_i8_blockscaled would write.  The row scale needs the row's maximum
+ * over every column tile, so the call runs the contraction twice: a first
+ * pass raises one integer maximum per row (atomicMax on the bit patterns of
+ * |y|), the second quantizes with the final scales.  It saves the f32
+ * output's memory and bytes, not MACs.
+ * Errors: as gemm_i8_blockscaled (I8G_EINVAL also for a null Q or s_out or
+ * ldq < N).
+ */
+int gemm_i8_requant(const int8_t* QA, int64_t lda, const float* s_row,
+                    const int8_t* QBt, int64_t ldb, const float* s_col,
+                    int64_t M, int64_t N, int64_t K, int8_t* Q, int64_t ldq,
+                    float* s_out, uint32_t flags, uint64_t* hash,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_i8_requant needs for this shape (>= 256). */
+size_t gemm_i8_requant_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /* Bytes of workspace output_hash needs (a constant, 256 + 16 KiB). */
 size_t output_hash_workspace_bytes(void);
 

@@ -26,7 +26,7 @@ import torch
 __all__ = ["quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "output_hash",
            "blockscaled_gemm", "hash_value", "workspace_bytes", "library_path", "load",
            "I8G_RELU", "I8G_HASH", "K_MAX", "I8GError", "quantize_rows_fmt", "quantize_cols_fmt",
-           "FMT_POW2", "FMT_INT4", "int4_line_bytes"]
+           "FMT_POW2", "FMT_INT4", "int4_line_bytes", "gemm_i8_requant"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libint8_gemm.so")
@@ -40,7 +40,8 @@ K_MAX = 133144
 EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_workspace_bytes",
             "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version",
             "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
-            "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt")
+            "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt",
+            "gemm_i8_requant", "gemm_i8_requant_workspace_bytes")
 
 _lib = None
 _ws = {}
@@ -77,6 +78,11 @@ def load():
     lib.gemm_i8_blockscaled.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                                         c_vp, c_i64, c_u32, c_vp, c_vp, c_sz, c_vp]
     lib.gemm_i8_blockscaled.restype = ctypes.c_int
+    lib.gemm_i8_requant.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
+                                    c_vp, c_i64, c_vp, c_u32, c_vp, c_vp, c_sz, c_vp]
+    lib.gemm_i8_requant.restype = ctypes.c_int
+    lib.gemm_i8_requant_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
+    lib.gemm_i8_requant_workspace_bytes.restype = c_sz
     lib.gemm_i8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
     lib.gemm_i8_workspace_bytes.restype = c_sz
     lib.output_hash.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
@@ -251,6 +257,29 @@ def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=
         _ptr(C), max(C.stride(0), N, 1), flags, _ptr(h), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(QA)))
     return (C, h) if want_hash else C
+
+
+def gemm_i8_requant(QA, s_row, QBt, s_col, relu=False, want_hash=False):
+    """The requantizing epilogue: (Q, scale) = quantize_rows of the GEMM's
+    f32 output, which is never stored; with want_hash also the output's
+    hash tensor."""
+    _req_matrix(QA, torch.int8, "QA")
+    _req_matrix(QBt, torch.int8, "QBt")
+    M, K = QA.shape
+    N, K2 = QBt.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: QA has {K}, QBt has {K2}")
+    dev = QA.device
+    Q = _int8_padded(M, N, dev)
+    s = torch.empty(M, dtype=torch.float32, device=dev)
+    h = torch.zeros(1, dtype=torch.int64, device=dev) if want_hash else None
+    ws = _workspace(dev, int(load().gemm_i8_requant_workspace_bytes(M, N, K)))
+    flags = (I8G_RELU if relu else 0) | (I8G_HASH if want_hash else 0)
+    _check(load().gemm_i8_requant(
+        _ptr(QA), QA.stride(0) if M > 0 else _round16(K), _ptr(s_row), _ptr(QBt),
+        QBt.stride(0) if N > 0 else _round16(K), _ptr(s_col), M, N, K, _ptr(Q), max(Q.stride(0), N, 1),
+        _ptr(s), flags, _ptr(h), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(QA)))
+    return (Q, s, h) if want_hash else (Q, s)
 
 
 def output_hash(C):

@@ -160,6 +160,75 @@ size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 size_t output_hash_workspace_bytes(void) { return kWsHeader + (size_t)kHashMaxParts * 8; }
 
+size_t gemm_i8_requant_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 256;
+  const GemmPlan plan = plan_gemm_requant(M, N, K > 0 ? K : 1);
+  return requant_rowmax_offset(plan) + (size_t)M * 4;
+}
+
+int gemm_i8_requant(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt, int64_t ldb,
+                    const float* s_col, int64_t M, int64_t N, int64_t K, int8_t* Q, int64_t ldq,
+                    float* s_out, uint32_t flags, uint64_t* hash, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const hipStream_t st = as_stream(stream);
+  if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX) return I8G_EINVAL;
+  if (flags & ~(I8G_RELU | I8G_HASH)) return I8G_EINVAL;
+  const bool want_hash = (flags & I8G_HASH) != 0;
+  if (want_hash && !hash) return I8G_EINVAL;
+  if (K > I8G_K_MAX) return I8G_EKRANGE;
+  if (!workspace || ((uintptr_t)workspace % 256) != 0 || workspace_bytes < kWsHeader) return I8G_EWORKSPACE;
+  if (M > 0 && !s_out) return I8G_EINVAL;
+  if (M == 0 || N == 0) {
+    // an M x 0 output: every row scale is the floor, no codes
+    if (M > 0) {
+      const int q = hip_status(launch_quantize_rows(nullptr, M, 0, 0, Q, ldq, s_out, 0, st));
+      if (q) return q;
+    }
+    if (want_hash) return hip_status(launch_output_hash(nullptr, M, N, N > 0 ? N : 1, hash, workspace, st));
+    return I8G_OK;
+  }
+  if (!Q || ldq < N || !s_row || !s_col) return I8G_EINVAL;
+  if (K > 0 && (!QA || !QBt)) return I8G_EINVAL;
+  const int64_t k16 = (K + 15) / 16 * 16;
+  if (K > 0 && (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < k16 ||
+                ldb < k16))
+    return I8G_EALIGN;
+  const GemmPlan plan = plan_gemm_requant(M, N, K > 0 ? K : 1);
+  const size_t rm_off = requant_rowmax_offset(plan);
+  if (workspace_bytes < rm_off + (size_t)M * 4) return I8G_EWORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  GemmParams p{};
+  p.A = QA;
+  p.B = QBt;
+  p.s_row = s_row;
+  p.s_col = s_col;
+  p.C = nullptr;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = N;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = plan.tiles_m;
+  p.tiles_n = plan.tiles_n;
+  p.splits = plan.splits;
+  p.k_per_split = plan.k_per_split;
+  p.relu = (flags & I8G_RELU) ? 1 : 0;
+  p.do_hash = want_hash ? 1 : 0;
+  p.stream_out = 0;
+  p.ticket = reinterpret_cast<unsigned int*>(ws);
+  p.hash_parts = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
+  p.n_shares = plan.hash_parts;
+  p.partials = nullptr;
+  p.comb_rows = plan.comb_rows;
+  p.hash_out = hash;
+  p.rowmax = reinterpret_cast<unsigned int*>(ws + rm_off);
+  p.Q = Q;
+  p.ldq = ldq;
+  p.s_out = s_out;
+  return hip_status(launch_gemm_requant(p, plan, st));
+}
+
 int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,
                         int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K, float* C,
                         int64_t ldc, uint32_t flags, uint64_t* hash, void* workspace,

@@ -154,7 +154,15 @@ __device__ __forceinline__ void store_out4(float* dst, float a, float b, float c
 // lane per row, so the lanes cover whole row segments.  The workgroup's
 // share of S is published last (hash_share_and_finalize).  With split-K the
 // raw int32 sums are stored instead, to the split's plane.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN>
+// MODE 0 writes C (or the split's partial plane); MODE 1 and 2 are the two
+// passes of the requantizing epilogue (GemmParams::rowmax): MODE 1 reduces
+// max |y| over the LPR lanes that hold a row and raises rowmax[row] with an
+// integer atomicMax on the bit pattern (non-negative floats order like their
+// bits, so the result is the exact row max in any order); MODE 2 turns the
+// final maxima into scales max(RN(a/127), RN(1e-8)) and writes
+// q = floor(RN(RN(y*RN(1/s)) + 0.5)) -- quantize_rows of the output, which
+// itself is never stored.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, int MODE = 0>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM][FN], int8_t* smem,
                                              int tm, int tn, int split) {
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -168,19 +176,29 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int M = p.M, N = p.N;
   const int col0 = tn * BN + wn * WTN;
-  const bool raw = p.splits > 1;
+  const bool raw = MODE == 0 && p.splits > 1;
   const bool relu = p.relu != 0;
   const bool stream = p.stream_out != 0;
 
   int* slab = reinterpret_cast<int*>(smem) + wave * SLAB;
   float* s_sr = reinterpret_cast<float*>(smem) + NWAVES * SLAB;
   unsigned int* s_rk = reinterpret_cast<unsigned int*>(s_sr + BM);
-  unsigned long long* s_red = reinterpret_cast<unsigned long long*>(s_rk + BM);   // NWAVES + 1 words
+  float* s_inv = reinterpret_cast<float*>(s_rk + BM);
+  unsigned long long* s_red = reinterpret_cast<unsigned long long*>(s_inv + BM);   // NWAVES + 1 words
   // row scales and row keys of the tile (zero beyond M: such rows add nothing)
   for (int r = tid; r < BM; r += NT) {
     const int gr = tm * BM + r;
     s_sr[r] = gr < M ? p.s_row[gr] : 0.0f;
     s_rk[r] = gr < M ? hash_row_key((unsigned int)gr) : 0u;
+    if (MODE == 2) {
+      float inv = 0.0f;
+      if (gr < M) {
+        const float sq = scale_of_absmax(__uint_as_float(p.rowmax[gr]));
+        inv = recip_rn(sq);
+        if (tn == 0) p.s_out[gr] = sq;
+      }
+      s_inv[r] = inv;
+    }
   }
   // this lane's four columns in the row-major read-back
   const int rr0 = lane / LPR, cc = (lane % LPR) * 4;
@@ -206,6 +224,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
   const int64_t ld = raw ? (int64_t)N : p.ldc;
   const bool vec = raw ? (N % 4 == 0) : ((p.ldc % 4 == 0) && (((uintptr_t)p.C & 15) == 0));
   int* part_base = raw ? p.partials + (int64_t)split * M * N : nullptr;
+  const bool qvec = MODE == 2 && (p.ldq % 4 == 0) && (((uintptr_t)p.Q & 3) == 0);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     park(i);
@@ -225,6 +244,43 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (gc0 + e < N) dst[e] = av[e];
+        }
+      } else if (MODE == 1) {
+        const float sr = s_sr[lr];
+        unsigned int mb = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float y = epilogue1(av[e], sr, sc[e]);   // 0 or -0 beyond N (scale 0)
+          if (relu) y = relu_pos0(y);
+          const unsigned int b = __float_as_uint(y) & 0x7FFFFFFFu;
+          mb = b > mb ? b : mb;
+        }
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) {
+          const unsigned int o = (unsigned int)__shfl_xor((int)mb, off, 64);
+          mb = o > mb ? o : mb;
+        }
+        if (lane % LPR == 0 && gr < M) atomicMax(p.rowmax + gr, mb);
+      } else if (MODE == 2) {
+        const float sr = s_sr[lr];
+        const uint64_t rk = s_rk[lr];
+        const float inv = s_inv[lr];
+        unsigned int packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float y = epilogue1(av[e], sr, sc[e]);
+          if (relu) y = relu_pos0(y);
+          tcol[e] += rk * (uint64_t)__float_as_uint(y);
+          packed |= ((unsigned int)quantize1(y, inv) & 0xFFu) << (8 * e);
+        }
+        if (gr >= M) continue;
+        int8_t* dst = p.Q + (int64_t)gr * p.ldq + gc0;
+        if (qvec && gc0 + 4 <= N) {
+          *reinterpret_cast<unsigned int*>(dst) = packed;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gc0 + e < N) dst[e] = (int8_t)((packed >> (8 * e)) & 0xFFu);
         }
       } else {
         const float sr = s_sr[lr];
@@ -248,7 +304,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, v16i (&acc)[FM
       }
     }
   }
-  if (!raw && p.do_hash) {
+  if (MODE != 1 && !raw && p.do_hash) {
     uint64_t hsum = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -265,7 +321,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 constexpr int dma_smem_bytes() {
   constexpr int NWAVES = WAVES_M * WAVES_N, WTN = BN / WAVES_N;
   constexpr int STAGE = (BM + BN) * BK;
-  constexpr int EPI_BYTES = NWAVES * 32 * (WTN + 8) * 4 + 2 * BM * 4 + 128;
+  constexpr int EPI_BYTES = NWAVES * 32 * (WTN + 8) * 4 + 3 * BM * 4 + 128;
   return STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
 }
 
@@ -435,7 +491,7 @@ __device__ __forceinline__ void dma_mainloop(
   __syncthreads();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE = 0>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_i8_dma_kernel(const GemmParams p) {
   constexpr int FM = BM / WAVES_M / 32, FN = BN / WAVES_N / 32;
@@ -447,7 +503,7 @@ gemm_i8_dma_kernel(const GemmParams p) {
   if (k_end > p.K) k_end = p.K;
   v16i acc[FM][FN];
   dma_mainloop<BM, BN, WAVES_M, WAVES_N, STAGES>(p, smem, tm, tn, k_begin, k_end, acc);
-  epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, tm, tn, split);
+  epilogue_lds<BM, BN, WAVES_M, WAVES_N, FM, FN, MODE>(p, acc, smem, tm, tn, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -1999,6 +2055,51 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
   }
   if (plan.splits > 1)
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(plan.comb_x, plan.comb_y), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// requantizing epilogue: zero the row maxima, pass 1 (row maxima), pass 2
+// (codes, scales, hash).  Both passes run the same tile walk and the same
+// exact contraction, so pass 2 sees exactly the y that pass 1 reduced.
+// ---------------------------------------------------------------------------
+__global__ void fill_zero_u32_kernel(unsigned int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K) {
+  int force = env_int("I8G_FORCE_TILE", -1);
+  if (force > 2) force = -1;
+  return plan_gemm_forced(M, N, K, false, force, 1);
+}
+
+size_t requant_rowmax_offset(const GemmPlan& plan) { return (plan.workspace_bytes + 255) / 256 * 256; }
+
+template <int MODE>
+static void launch_dma_mode(const GemmParams& p, int cfg, unsigned int grid, hipStream_t stream) {
+  switch (cfg) {
+    case 0:
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 4, 4, MODE>), dim3(grid), dim3(512), 0, stream, p);
+      break;
+    case 1:
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 128, 2, 2, 4, MODE>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<128, 128, 2, 2, 4, MODE>), dim3(grid), dim3(256), 0, stream, p);
+      break;
+  }
+}
+
+hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned int)((p.M + 255) / 256)), dim3(256), 0, stream,
+                     p.rowmax, p.M);
+  const int do_hash = p.do_hash;
+  p.do_hash = 0;
+  launch_dma_mode<1>(p, plan.cfg, (unsigned int)plan.grid, stream);
+  p.do_hash = do_hash;
+  launch_dma_mode<2>(p, plan.cfg, (unsigned int)plan.grid, stream);
   return hipGetLastError();
 }
 

@@ -25,6 +25,13 @@ struct GemmParams {
   int comb_rows;                    // rows per split-K combine workgroup
   uint64_t* hash_out;
   int a4, b4;                       // operand stored as int4, two per byte (gemm_i4_kernel only)
+  // requantizing epilogue (gemm_i8_requant): pass 1 only raises rowmax[i]
+  // to the largest |y| bit pattern of row i; pass 2 writes the int8 codes of
+  // y with the row scales those maxima give
+  unsigned int* rowmax;             // M words, zero before pass 1
+  int8_t* Q;                        // pass 2: codes, row-major, leading dimension ldq
+  int64_t ldq;
+  float* s_out;                     // pass 2: the M row scales of the codes
 };
 
 struct GemmPlan {
@@ -64,6 +71,11 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
 // I8G_FORCE_SPLITS).
 GemmPlan plan_gemm_int4(int64_t M, int64_t N, int64_t K, int force_splits);
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
+// Requantizing epilogue: one K split, a non-persistent tile (I8G_FORCE_TILE
+// 0..2 honoured for tests); the workspace adds M words of row maxima.
+GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K);
+size_t requant_rowmax_offset(const GemmPlan& plan);
+hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, hipStream_t stream);
 
 // fmt: FMT_POW2 / FMT_INT4 bits (i8g_device.h); int4 outputs take
 // 16*ceil(len/32) bytes per line, 16-byte aligned.

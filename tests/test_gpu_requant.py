@@ -1,0 +1,115 @@
+"""GPU parity of the requantizing epilogue (gemm_i8_requant) against the
+oracle (oracle/requant.py: quantize_rows of the method's output) and against
+the library's own two-call path, bit for bit, with the hash of the f32 output
+that the call never stores."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hashref, ref, requant
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[requant]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def g():
+    import int8_gemm_amd as g
+    g.load()
+    return g
+
+
+def _operands(g, M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    A = rng.standard_t(3, (M, K)).astype(np.float32)
+    B = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    if M > 4:
+        A[3] = 0.0                     # zero row: floor scale downstream
+    QA, sA = ref.quantize_rows(A)
+    QB, sB = ref.quantize_cols(B)
+    dQA, dsA = g.quantize_rows(torch.from_numpy(A).cuda())
+    dQB, dsB = g.quantize_cols(torch.from_numpy(B).cuda())
+    return (QA, sA, QB, sB), (dQA, dsA, dQB, dsB)
+
+
+SHAPES = [(1, 1, 1), (17, 33, 15), (130, 190, 70), (300, 520, 192), (256, 200, 768), (64, 64, 4096),
+          (129, 1000, 33)]
+
+
+@pytest.mark.parametrize("relu", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_requant_matches_oracle(g, shape, relu):
+    M, N, K = shape
+    say("requant", M, N, K, relu)
+    (QA, sA, QB, sB), dev = _operands(g, M, N, K, M + N + K)
+    Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, relu)
+    Q, s, h = g.gemm_i8_requant(*dev, relu=relu, want_hash=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(Q.cpu().numpy(), Qw)
+    assert g.hash_value(h) == hashref.output_hash(Cw)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_requant_every_tile(g, tile):
+    M, N, K = 300, 700, 200
+    say("requant tile", tile)
+    (QA, sA, QB, sB), dev = _operands(g, M, N, K, 77)
+    Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, True)
+    os.environ["I8G_FORCE_TILE"] = str(tile)
+    try:
+        Q, s, h = g.gemm_i8_requant(*dev, relu=True, want_hash=True)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["I8G_FORCE_TILE"]
+    assert np.array_equal(Q.cpu().numpy(), Qw) and np.array_equal(s.cpu().numpy(), sw)
+    assert g.hash_value(h) == hashref.output_hash(Cw)
+
+
+def test_requant_mlp_up_full_size(g):
+    """GPT-2-small MLP up-projection 8192x3072x768 with ReLU: the codes and
+    scales equal quantize_rows of the library's own f32 output and the
+    oracle's; the hash equals the oracle's hash of the f32 output."""
+    from synth import inputs as S
+    X, Wu, _ = S.w2_inputs()
+    say("requant mlp up full size")
+    dQA, dsA = g.quantize_rows(torch.from_numpy(X).cuda())
+    dQB, dsB = g.quantize_cols(torch.from_numpy(Wu).cuda())
+    Q, s, h = g.gemm_i8_requant(dQA, dsA, dQB, dsB, relu=True, want_hash=True)
+    C, h2 = g.gemm_i8_blockscaled(dQA, dsA, dQB, dsB, relu=True, want_hash=True)
+    Q2, s2 = g.quantize_rows(C)
+    torch.cuda.synchronize()
+    assert torch.equal(Q, Q2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
+    assert g.hash_value(h) == g.hash_value(h2)
+    QA, sA = ref.quantize_rows(X)
+    QB, sB = ref.quantize_cols(Wu)
+    Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, True)
+    assert np.array_equal(Q.cpu().numpy(), Qw) and np.array_equal(s.cpu().numpy(), sw)
+    assert g.hash_value(h) == hashref.output_hash(Cw)
+
+
+def test_requant_empty(g):
+    lib = g.load()
+    dev = torch.device("cuda")
+    s = torch.full((5,), -1.0, device=dev)
+    h = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+    Q = torch.empty((5, 16), dtype=torch.int8, device=dev)
+    A = torch.zeros((5, 16), dtype=torch.int8, device=dev)
+    sa = torch.ones(5, device=dev)
+    rc = lib.gemm_i8_requant(A.data_ptr(), 16, sa.data_ptr(), None, 16, None, 5, 0, 7, Q.data_ptr(), 16,
+                             s.data_ptr(), 2, h.data_ptr(), ws.data_ptr(), 256, None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert np.all(s.cpu().numpy() == ref.SCALE_FLOOR)
+    assert g.hash_value(h) == hashref.output_hash(np.zeros((5, 0), dtype=np.float32))
+    # argument errors
+    assert lib.gemm_i8_requant(A.data_ptr(), 16, sa.data_ptr(), A.data_ptr(), 16, sa.data_ptr(), 5, 5, 7,
+                               Q.data_ptr(), 4, s.data_ptr(), 0, None, ws.data_ptr(), 256, None) == 1
+    assert lib.gemm_i8_requant(A.data_ptr(), 16, sa.data_ptr(), A.data_ptr(), 16, sa.data_ptr(), 5, 5, 7,
+                               Q.data_ptr(), 16, s.data_ptr(), 4, None, ws.data_ptr(), 256, None) == 1
