@@ -2,7 +2,7 @@
 """Throughput of the bit-exact block-scaled int8 GEMM path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload mlp|head|step|w1]
-                    [--b-format int8|pow2|int4|int4-pow2]
+                    [--b-format int8|pow2|int4|int4-pow2] [--requant]
 
 One step is one pass of the whole path over one batch: per GEMM, the
 quantize pass of each operand (per row, or per column with the transposed
@@ -21,6 +21,8 @@ launches of that call; `cpu_baseline` = the CPU oracle timed on this host;
 `parity` = whether the oracle's output hashes equal the GPU's.
 --b-format stores every B operand in one of the presk page's "Integer
 weights" formats (the headline line uses the default int8 / absmax).
+--requant lets a GEMM whose output is the next GEMM's per-row quantized
+operand write those codes and scales itself (gemm_i8_requant).
 """
 import argparse
 import hashlib
@@ -110,7 +112,7 @@ def int4_line_bytes(n):
 
 
 class GpuStep:
-    def __init__(self, g, torch, tensors, gemms, fmt_b=0):
+    def __init__(self, g, torch, tensors, gemms, fmt_b=0, requant=False):
         self.g, self.torch, self.lib = g, torch, g.load()
         dev = torch.device("cuda:0")
         self.dev = dev
@@ -137,6 +139,21 @@ class GpuStep:
             self.t[e["out"]] = e["C"]
             ws_bytes = max(ws_bytes, g.workspace_bytes(M, N, K))
             self.gemms.append(e)
+        # requantizing epilogue: a GEMM whose output is the per-row quantized A
+        # operand of a later GEMM writes that GEMM's codes and scales itself
+        # (gemm_i8_requant) and the later GEMM skips its quantize_A
+        for e in self.gemms:
+            e["requant_into"] = None
+            e["skip_qa"] = False
+        if requant:
+            for i, e in enumerate(self.gemms):
+                for e2 in self.gemms[i + 1:]:
+                    if e2["a_key"] == e["out"] and e2["a_mode"] == "rows":
+                        e["requant_into"] = e2
+                        e2["skip_qa"] = True
+                        ws_bytes = max(ws_bytes, int(self.lib.gemm_i8_requant_workspace_bytes(
+                            e["M"], e["N"], e["K"])))
+                        break
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
 
     def _q(self, mode, X, Q, s, ld, fmt=0):
@@ -156,12 +173,29 @@ class GpuStep:
         if rc:
             raise RuntimeError(self.lib.i8g_status_string(rc).decode())
 
+    def _requant(self, e):
+        e2 = e["requant_into"]
+        flags = (1 if e["relu"] else 0) | 2
+        rc = self.lib.gemm_i8_requant(e["QA"].data_ptr(), e["ld"], e["sA"].data_ptr(),
+                                      e["QB"].data_ptr(), e["ldb"], e["sB"].data_ptr(),
+                                      e["M"], e["N"], e["K"], e2["QA"].data_ptr(), e2["ld"],
+                                      e2["sA"].data_ptr(), flags, e["h"].data_ptr(),
+                                      self.ws.data_ptr(), self.ws.numel(), self.sp)
+        if rc:
+            raise RuntimeError(self.lib.i8g_status_string(rc).decode())
+
     def calls(self, e):
-        """The three calls of one GEMM of the step, as (label, function)."""
-        return (("quantize_A", lambda: self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])),
-                ("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ldb"],
-                                               self.fmt_b)),
-                ("gemm", lambda: self._gemm(e)))
+        """The calls of one GEMM of the step, as (label, function)."""
+        out = []
+        if not e["skip_qa"]:
+            out.append(("quantize_A", lambda: self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])))
+        out.append(("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ldb"],
+                                                  self.fmt_b)))
+        if e["requant_into"] is not None:
+            out.append(("requant", lambda: self._requant(e)))
+        else:
+            out.append(("gemm", lambda: self._gemm(e)))
+        return out
 
     def run(self):
         """Enqueue one step on torch's current stream (a graph capture switches
@@ -272,6 +306,9 @@ def main():
     ap.add_argument("--b-format", default="int8", choices=list(B_FORMATS),
                     help="storage format of every B operand (int4: two values per byte; "
                          "pow2: power-of-two scales); A operands stay int8 with absmax scales")
+    ap.add_argument("--requant", action="store_true",
+                    help="a GEMM whose output feeds the next GEMM's per-row quantize writes int8 "
+                         "codes and scales directly (gemm_i8_requant; the f32 output is not stored)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the step captured in a HIP graph")
@@ -292,7 +329,7 @@ def main():
     log(f"[bench] workload {a.workload}: generating inputs")
     desc, tensors, gemms = make_workload(a.workload)
     fmt_b = B_FORMATS[a.b_format]
-    step = GpuStep(g, torch, tensors, gemms, fmt_b)
+    step = GpuStep(g, torch, tensors, gemms, fmt_b, a.requant)
     if a.copy_probe > 0:
         src = torch.ones(a.copy_probe << 18, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -380,10 +417,11 @@ def main():
         e = next(x for x in step.gemms if x["name"] == name)
         avg = statistics.mean(us)
         M, N, K = e["M"], e["N"], e["K"]
-        if label == "gemm":
+        if label in ("gemm", "requant"):
             gops = 2.0 * M * N * K
             b_bytes = N * int4_line_bytes(K) if fmt_b & 2 else N * K
-            nbytes = M * K + b_bytes + 4 * M + 4 * N + 4 * M * N + 8
+            out_bytes = 4 * M * N if label == "gemm" else M * N + 4 * M   # f32, or int8 + scales
+            nbytes = M * K + b_bytes + 4 * M + 4 * N + out_bytes + 8
             bound = "mfma" if gops / nbytes >= RIDGE else "hbm"
             shape = f"{M}x{N}x{K}"
         else:
@@ -431,7 +469,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": desc, "name": a.workload, "b_format": a.b_format,
+        "config": {"workload": desc, "name": a.workload, "b_format": a.b_format, "requant": a.requant,
                    "gemms": [f"{e['M']}x{e['N']}x{e['K']}{' relu' if e['relu'] else ''}"
                              for e in step.gemms],
                    "int8_ops_per_step": ops, "batch": 8, "seq_len": 1024, "tokens": 8192},
