@@ -155,6 +155,24 @@ class GpuStep:
                             e["M"], e["N"], e["K"])))
                         break
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        # the quantize passes of input tensors (not of a GEMM's output) depend
+        # on nothing in the step: they go first, together, as one
+        # quantize_batch call
+        self.inputs = set(tensors)
+        specs, self.batched = [], []
+        for e in self.gemms:
+            if not e["skip_qa"] and e["a_key"] in self.inputs:
+                specs.append((self.t[e["a_key"]], e["a_mode"] == "cols", 0, e["QA"], e["ld"], e["sA"]))
+                self.batched.append((e["name"], "quantize_A"))
+            if e["b_key"] in self.inputs:
+                specs.append((self.t[e["b_key"]], e["b_mode"] == "cols", self.fmt_b, e["QB"], e["ldb"], e["sB"]))
+                self.batched.append((e["name"], "quantize_B"))
+        self.jobs = (g.QuantizeJob * max(1, len(specs)))()
+        for i, (X, by_col, fmt, Q, ldq, s) in enumerate(specs):
+            rows, cols = X.shape
+            self.jobs[i] = g.QuantizeJob(X.data_ptr(), rows, cols, X.stride(0), Q.data_ptr(), ldq,
+                                         s.data_ptr(), 1 if by_col else 0, fmt)
+        self.njobs = len(specs)
 
     def _q(self, mode, X, Q, s, ld, fmt=0):
         rows, cols = X.shape
@@ -184,13 +202,22 @@ class GpuStep:
         if rc:
             raise RuntimeError(self.lib.i8g_status_string(rc).decode())
 
-    def calls(self, e):
-        """The calls of one GEMM of the step, as (label, function)."""
+    def _batch(self):
+        rc = self.lib.quantize_batch(self.jobs, self.njobs, self.sp)
+        if rc:
+            raise RuntimeError(self.lib.i8g_status_string(rc).decode())
+
+    def calls(self, e, batched=False):
+        """The calls of one GEMM of the step, as (label, function); with
+        batched=True the input quantize passes, which quantize_batch makes,
+        are left out."""
         out = []
-        if not e["skip_qa"]:
+        skip = set(lab for name, lab in self.batched if name == e["name"]) if batched else set()
+        if not e["skip_qa"] and "quantize_A" not in skip:
             out.append(("quantize_A", lambda: self._q(e["a_mode"], self.t[e["a_key"]], e["QA"], e["sA"], e["ld"])))
-        out.append(("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"], e["ldb"],
-                                                  self.fmt_b)))
+        if "quantize_B" not in skip:
+            out.append(("quantize_B", lambda: self._q(e["b_mode"], self.t[e["b_key"]], e["QB"], e["sB"],
+                                                      e["ldb"], self.fmt_b)))
         if e["requant_into"] is not None:
             out.append(("requant", lambda: self._requant(e)))
         else:
@@ -202,8 +229,10 @@ class GpuStep:
         it, so it is read at every call)."""
         self.stream = self.torch.cuda.current_stream(self.dev)
         self.sp = self.stream.cuda_stream
+        if self.njobs:
+            self._batch()
         for e in self.gemms:
-            for _, fn in self.calls(e):
+            for _, fn in self.calls(e, batched=True):
                 fn()
 
     def hashes(self):
@@ -410,6 +439,20 @@ def main():
             e1.record(step.stream)
             torch.cuda.synchronize()
             per[(e["name"], label)] = [e0.elapsed_time(e1) * 1e3 / reps]
+    batch_us = None
+    if step.njobs:
+        # the batched input passes as the step issues them (one call)
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(2_000_000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(step.stream)
+        for _ in range(reps):
+            step._batch()
+        e1.record(step.stream)
+        torch.cuda.synchronize()
+        batch_us = e0.elapsed_time(e1) * 1e3 / reps
     if step.hashes() != gpu_hashes:
         raise SystemExit("repeated calls changed the output hashes")
     kernels = []
@@ -443,6 +486,15 @@ def main():
                         "frac": round(ach / peak, 4), "algorithmic_bytes": nbytes,
                         "int8_ops": gops,
                         "tops": round(gops / (avg * 1e-6) / 1e12, 1) if gops else None})
+    if batch_us is not None:
+        # the batch runs the input passes timed one by one above; its bytes
+        # are theirs (it is not a single kernel, so it is not a roofline candidate)
+        parts = [k for k in kernels if tuple(k["call"].rsplit(".", 1)) in set(step.batched)]
+        nbytes = sum(k["algorithmic_bytes"] for k in parts)
+        batch_entry = {"call": "inputs.quantize_batch", "passes": len(parts), "avg_us": round(batch_us, 2),
+                       "sum_of_single_calls_us": round(sum(k["avg_us"] for k in parts), 2),
+                       "achieved": round(nbytes / (batch_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                       "algorithmic_bytes": nbytes}
     dom = max(kernels, key=lambda k: k["avg_us"])
     roof = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
             "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic_for(dom["call"]),
@@ -476,6 +528,7 @@ def main():
         "pct_of_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
         "roofline": roof,
         "kernels": kernels,
+        "quantize_batch": batch_entry if batch_us is not None else None,
         "cpu_baseline": cpu,
         "parity": parity,
         "gpu_hashes": [f"{h:#018x}" for h in gpu_hashes],

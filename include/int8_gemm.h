@@ -137,6 +137,33 @@ int quantize_cols_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                       int8_t* Qt, int64_t ldqt, float* scale, uint32_t format, void* stream);
 
 /*
+ * quantize_batch -- n independent quantize passes enqueued together: the
+ * int8 passes that fit one kernel run in a single launch (24 at most per
+ * launch) and share the chip, which matters for the many small passes of a
+ * step (weights, skinny activations) whose time is mostly latency; the
+ * others (int4 formats, column passes over more than 8192 rows) are
+ * enqueued one by one on the same stream.  Every output is byte for byte
+ * that of the single call.
+ *   jobs  host array of n descriptions; by_col = 0 is quantize_rows_fmt,
+ *         by_col = 1 quantize_cols_fmt, with the same arguments and rules.
+ *         No job may write memory another job reads or writes.
+ * Errors: the first failing job's status from validating all of them;
+ * nothing is enqueued unless every job is valid.  I8G_EINVAL for n < 0 or a
+ * null array with n > 0; I8G_EHIP.
+ */
+typedef struct i8g_quantize_job {
+  const float* X;
+  int64_t rows, cols, ldx;
+  int8_t* Q;
+  int64_t ldq;
+  float* scale;
+  uint32_t by_col;
+  uint32_t format;
+} i8g_quantize_job;
+
+int quantize_batch(const i8g_quantize_job* jobs, int32_t n, void* stream);
+
+/*
  * gemm_i8_blockscaled -- C = epilogue(QA . QBt^T) (steps 2 and 3 of "The
  * verified INT8 units").
  *   QA     M x K int8, row-major (K contiguous), leading dimension lda.

@@ -26,7 +26,7 @@ import torch
 __all__ = ["quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "output_hash",
            "blockscaled_gemm", "hash_value", "workspace_bytes", "library_path", "load",
            "I8G_RELU", "I8G_HASH", "K_MAX", "I8GError", "quantize_rows_fmt", "quantize_cols_fmt",
-           "FMT_POW2", "FMT_INT4", "int4_line_bytes", "gemm_i8_requant"]
+           "FMT_POW2", "FMT_INT4", "int4_line_bytes", "gemm_i8_requant", "quantize_batch"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libint8_gemm.so")
@@ -41,7 +41,7 @@ EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_wo
             "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version",
             "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
             "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt",
-            "gemm_i8_requant", "gemm_i8_requant_workspace_bytes")
+            "gemm_i8_requant", "gemm_i8_requant_workspace_bytes", "quantize_batch")
 
 _lib = None
 _ws = {}
@@ -78,6 +78,8 @@ def load():
     lib.gemm_i8_blockscaled.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                                         c_vp, c_i64, c_u32, c_vp, c_vp, c_sz, c_vp]
     lib.gemm_i8_blockscaled.restype = ctypes.c_int
+    lib.quantize_batch.argtypes = [ctypes.POINTER(QuantizeJob), ctypes.c_int32, c_vp]
+    lib.quantize_batch.restype = ctypes.c_int
     lib.gemm_i8_requant.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                                     c_vp, c_i64, c_vp, c_u32, c_vp, c_vp, c_sz, c_vp]
     lib.gemm_i8_requant.restype = ctypes.c_int
@@ -131,7 +133,7 @@ def _req_matrix(x, dtype, name):
         raise ValueError(f"{name} must have dtype {dtype}, got {x.dtype}")
     if not x.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
-    if x.size(1) > 1 and x.stride(1) != 1:
+    if x.numel() > 0 and x.size(1) > 1 and x.stride(1) != 1:   # (empty tensors may carry stride 0)
         raise ValueError(f"{name} must be row-major (unit column stride)")
 
 
@@ -203,6 +205,41 @@ def quantize_cols_fmt(X, fmt):
     _check(load().quantize_cols_fmt(_ptr(X), rows, cols, _ld(X), _ptr(Qt), Qt.stride(0), _ptr(s),
                                     fmt, _stream(X)))
     return Qt, s
+
+
+class QuantizeJob(ctypes.Structure):
+    """i8g_quantize_job (include/int8_gemm.h)."""
+    _fields_ = [("X", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("Q", ctypes.c_void_p), ("ldq", ctypes.c_int64),
+                ("scale", ctypes.c_void_p), ("by_col", ctypes.c_uint32), ("format", ctypes.c_uint32)]
+
+
+def quantize_jobs(specs):
+    """ctypes job array and outputs for specs = [(X, by_col, fmt), ...]:
+    returns (array, [(Q, scale), ...]) with outputs laid out as the single
+    calls lay them out."""
+    arr = (QuantizeJob * len(specs))()
+    outs = []
+    for i, (X, by_col, fmt) in enumerate(specs):
+        _req_matrix(X, torch.float32, "X")
+        rows, cols = X.shape
+        lines, n = (cols, rows) if by_col else (rows, cols)
+        Q = _line_buffer(lines, n, fmt, X.device)
+        s = torch.empty(lines, dtype=torch.float32, device=X.device)
+        arr[i] = QuantizeJob(X.data_ptr(), rows, cols, _ld(X), Q.data_ptr(), Q.stride(0), s.data_ptr(),
+                             1 if by_col else 0, fmt)
+        outs.append((Q, s))
+    return arr, outs
+
+
+def quantize_batch(specs):
+    """Several quantize passes in one call: specs = [(X, by_col, fmt), ...];
+    returns [(Q, scale), ...], each equal to quantize_{rows,cols}_fmt(X, fmt)."""
+    if not specs:
+        return []
+    arr, outs = quantize_jobs(specs)
+    _check(load().quantize_batch(arr, len(specs), _stream(specs[0][0])))
+    return outs
 
 
 def workspace_bytes(M, N, K):

@@ -3,6 +3,8 @@
 // on the caller's stream.  No device memory is allocated here.
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/int8_gemm.h"
 #include "i8g_device.h"
 #include "i8g_launch.h"
@@ -14,17 +16,6 @@ namespace {
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? I8G_OK : I8G_EHIP; }
-
-int check_quantize_args(const float* X, int64_t rows, int64_t cols, int64_t ldx, const void* Q,
-                        int64_t ldq_min_ok, int64_t ldq, const float* scale) {
-  if (rows < 0 || cols < 0) return I8G_EINVAL;
-  if (rows > INT32_MAX || cols > INT32_MAX) return I8G_EINVAL;
-  if (rows == 0) return I8G_OK;
-  if (cols == 0) return scale ? I8G_OK : I8G_EINVAL;
-  if (!X || !Q || !scale) return I8G_EINVAL;
-  if (ldx < cols || ldq < ldq_min_ok) return I8G_EINVAL;
-  return I8G_OK;
-}
 
 }  // namespace
 
@@ -112,28 +103,72 @@ const char* i8g_status_string(int status) {
 
 const char* i8g_version(void) { return "int8_gemm 0.1.0 gfx950"; }
 
+// Validates one quantize pass (quantize_rows_fmt when by_col == 0, else
+// quantize_cols_fmt); *work is set when there is something to enqueue.  A
+// pass over lines of length 0 still writes the floor scale of each line.
+static int check_fmt_args(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Q,
+                          int64_t ldq, const float* scale, bool by_col, uint32_t format, bool* work) {
+  *work = false;
+  if (format & ~(I8G_FMT_POW2 | I8G_FMT_INT4)) return I8G_EINVAL;
+  if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return I8G_EINVAL;
+  const bool int4 = (format & I8G_FMT_INT4) != 0;
+  const int64_t lines = by_col ? cols : rows, len = by_col ? rows : cols;
+  const int64_t line_bytes = int4 ? (len + 31) / 32 * 16 : len;
+  if (lines == 0) return I8G_OK;
+  if (!scale) return I8G_EINVAL;
+  if (len > 0) {
+    if (!X || !Q) return I8G_EINVAL;
+    if (ldx < cols || ldq < line_bytes) return I8G_EINVAL;
+    if (int4 && (((uintptr_t)Q % 16) || (ldq % 16))) return I8G_EALIGN;
+  }
+  *work = true;
+  return I8G_OK;
+}
+
 int quantize_rows_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q,
                       int64_t ldq, float* scale, uint32_t format, void* stream) {
-  if (format & ~(I8G_FMT_POW2 | I8G_FMT_INT4)) return I8G_EINVAL;
-  const bool int4 = (format & I8G_FMT_INT4) != 0;
-  const int64_t line_bytes = int4 ? (cols + 31) / 32 * 16 : cols;
-  int st = check_quantize_args(X, rows, cols, ldx, Q, line_bytes, ldq, scale);
-  if (st != I8G_OK || rows == 0) return st;
-  if (cols == 0 && !scale) return I8G_EINVAL;   // empty rows still get the floor scale
-  if (int4 && cols > 0 && (((uintptr_t)Q % 16) || (ldq % 16))) return I8G_EALIGN;
+  bool work = false;
+  const int st = check_fmt_args(X, rows, cols, ldx, Q, ldq, scale, false, format, &work);
+  if (st != I8G_OK || !work) return st;
   return hip_status(launch_quantize_rows(X, rows, cols, ldx, Q, ldq, scale, (int)format, as_stream(stream)));
 }
 
 int quantize_cols_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
                       int64_t ldqt, float* scale, uint32_t format, void* stream) {
-  if (format & ~(I8G_FMT_POW2 | I8G_FMT_INT4)) return I8G_EINVAL;
-  const bool int4 = (format & I8G_FMT_INT4) != 0;
-  const int64_t line_bytes = int4 ? (rows + 31) / 32 * 16 : rows;
-  int st = check_quantize_args(X, rows, cols, ldx, Qt, line_bytes, ldqt, scale);
-  if (st != I8G_OK || cols == 0) return st;
-  if (rows == 0 && !scale) return I8G_EINVAL;   // empty columns still get the floor scale
-  if (int4 && rows > 0 && (((uintptr_t)Qt % 16) || (ldqt % 16))) return I8G_EALIGN;
+  bool work = false;
+  const int st = check_fmt_args(X, rows, cols, ldx, Qt, ldqt, scale, true, format, &work);
+  if (st != I8G_OK || !work) return st;
   return hip_status(launch_quantize_cols(X, rows, cols, ldx, Qt, ldqt, scale, (int)format, as_stream(stream)));
+}
+
+int quantize_batch(const i8g_quantize_job* jobs, int32_t n, void* stream) {
+  if (n < 0 || (n > 0 && !jobs)) return I8G_EINVAL;
+  const hipStream_t st = as_stream(stream);
+  // validate everything before enqueueing anything
+  std::vector<char> work((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const i8g_quantize_job& j = jobs[i];
+    bool w = false;
+    const int s = check_fmt_args(j.X, j.rows, j.cols, j.ldx, j.Q, j.ldq, j.scale, j.by_col != 0, j.format, &w);
+    if (s != I8G_OK) return s;
+    work[i] = w ? 1 : 0;
+  }
+  std::vector<QJob> batch;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!work[i]) continue;
+    const i8g_quantize_job& j = jobs[i];
+    QJob q{};
+    if (plan_qjob(j.X, j.rows, j.cols, j.ldx, j.Q, j.ldq, j.scale, j.by_col != 0, (int)j.format, q)) {
+      batch.push_back(q);
+      continue;
+    }
+    const hipError_t e = j.by_col
+        ? launch_quantize_cols(j.X, j.rows, j.cols, j.ldx, j.Q, j.ldq, j.scale, (int)j.format, st)
+        : launch_quantize_rows(j.X, j.rows, j.cols, j.ldx, j.Q, j.ldq, j.scale, (int)j.format, st);
+    if (e != hipSuccess) return I8G_EHIP;
+  }
+  if (batch.empty()) return I8G_OK;
+  return hip_status(launch_quantize_batch(batch.data(), (int)batch.size(), st));
 }
 
 int quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,

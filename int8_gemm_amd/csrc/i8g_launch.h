@@ -83,6 +83,26 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
                                 int8_t* Q, int64_t ldq, float* scale, int fmt, hipStream_t stream);
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                 int8_t* Qt, int64_t ldqt, float* scale, int fmt, hipStream_t stream);
+// One quantize pass of quantize_batch (planned by plan_qjob).
+struct QJob {
+  const float* X;
+  int8_t* Q;
+  float* scale;
+  int64_t rows, cols, ldx, ldq;
+  int kind, param, fmt, vec_in, vec_out;
+  int blocks;   // workgroups of 1024 threads the pass takes
+  int first;    // first workgroup id of its range in the launch
+};
+constexpr int kQBatchMax = 24;   // jobs per launch (kernel argument space)
+struct QBatch {
+  QJob job[kQBatchMax];
+  int n;
+};
+// Fills q for an int8 pass the batch kernel can run (false: int4 formats,
+// empty shapes, and tall column passes that need several kernels).
+bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
+               float* scale, bool by_col, int fmt, QJob& q);
+hipError_t launch_quantize_batch(QJob* jobs, int n, hipStream_t stream);
 hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
                               uint64_t* hash, void* workspace, hipStream_t stream);
 

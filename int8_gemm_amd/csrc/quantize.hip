@@ -65,13 +65,16 @@ __device__ __forceinline__ void store4(int8_t* row, int64_t c, int64_t cols, uns
 // ---------------------------------------------------------------------------
 // rows: one wavefront per row, VPL groups of 4 elements per lane in registers
 // ---------------------------------------------------------------------------
+// The kernel bodies take the workgroup's index within their own grid (`bid`)
+// and their LDS from the caller, so that quantize_batch_kernel can run
+// several of them in one launch.
 template <int VPL, int FMT>
-__global__ void __launch_bounds__(256)
-qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
-                  int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
-                  int vec_out) {
+__device__ __forceinline__ void qrows_wave_body(const float* __restrict__ X, int64_t rows, int64_t cols,
+                                                int64_t ldx, int8_t* __restrict__ Q, int64_t ldq,
+                                                float* __restrict__ scale, int vec_in, int vec_out,
+                                                int64_t bid) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t r = bid * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);   // a wave per row
   if (r >= rows) return;
   const float* xr = X + r * ldx;
   float4 v[VPL];
@@ -93,19 +96,26 @@ qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
   }
 }
 
+template <int VPL, int FMT>
+__global__ void __launch_bounds__(256)
+qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                  int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
+                  int vec_out) {
+  qrows_wave_body<VPL, FMT>(X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // rows: one 1024-thread workgroup per row (long rows)
 // ---------------------------------------------------------------------------
 template <int VPT, int FMT>
-__global__ void __launch_bounds__(1024)
-qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
-                   int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
-                   int vec_out) {
+__device__ __forceinline__ void qrows_block_body(const float* __restrict__ X, int64_t rows, int64_t cols,
+                                                 int64_t ldx, int8_t* __restrict__ Q, int64_t ldq,
+                                                 float* __restrict__ scale, int vec_in, int vec_out,
+                                                 int64_t bid, float* red /* LDS, 16 floats */) {
   constexpr int NT = 1024;
   constexpr int64_t CHUNK = (int64_t)NT * VPT * 4;
-  __shared__ float red[NT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t r = blockIdx.x;
+  const int64_t r = bid;
   const float* xr = X + r * ldx;
   int8_t* qr = Q + r * ldq;
   float4 v[VPT];
@@ -146,12 +156,35 @@ qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
   }
 }
 
+template <int VPT, int FMT>
+__global__ void __launch_bounds__(1024)
+qrows_block_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                   int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
+                   int vec_out) {
+  __shared__ float red[16];
+  qrows_block_body<VPT, FMT>(X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out, blockIdx.x, red);
+}
+
+// Row path by row length: a wave per row with VPL float4 per lane up to 4096
+// values, else a 1024-thread workgroup per row (VPT float4 per thread).
+static int rows_wave_vpl(int64_t cols) {
+  if (cols <= 256) return 1;
+  if (cols <= 512) return 2;
+  if (cols <= 768) return 3;
+  if (cols <= 1024) return 4;
+  if (cols <= 2048) return 8;
+  if (cols <= 3072) return 12;
+  if (cols <= 4096) return 16;
+  return 0;
+}
+static int rows_block_vpt(int64_t cols) { return cols <= 1024 * 8 * 4 ? 8 : 16; }
+
 template <int FMT>
 hipError_t quantize_rows_int8(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                               int8_t* Q, int64_t ldq, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
-  if (cols <= 256 * 16) {
+  if (rows_wave_vpl(cols) > 0) {
     const dim3 grid((unsigned int)((rows + 3) / 4)), block(256);
     if (cols <= 256)
       hipLaunchKernelGGL((qrows_wave_kernel<1, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
@@ -169,7 +202,7 @@ hipError_t quantize_rows_int8(const float* X, int64_t rows, int64_t cols, int64_
       hipLaunchKernelGGL((qrows_wave_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
   } else {
     const dim3 grid((unsigned int)rows), block(1024);
-    if (cols <= 1024 * 8 * 4)
+    if (rows_block_vpt(cols) == 8)
       hipLaunchKernelGGL((qrows_block_kernel<8, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else
       hipLaunchKernelGGL((qrows_block_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
@@ -317,19 +350,22 @@ __device__ __forceinline__ int xcd_grouped(int wg, int total) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
+// LDS of qcols_reg_body: the transposed tile, then the column maxima of the
+// 16 waves, then the reciprocals.
+constexpr int QCR_SMEM_BYTES = QCR_MAX_ELEMS + (QCR_THREADS / 64) * 64 * 4 + 64 * 4;
+
 template <int BC, int FMT>
-__global__ void __launch_bounds__(QCR_THREADS)
-qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
-                 int8_t* __restrict__ Qt, int64_t ldqt, float* __restrict__ scale, int vec_in,
-                 int vec_out) {
+__device__ __forceinline__ void qcols_reg_body(const float* __restrict__ X, int64_t rows, int64_t cols,
+                                               int64_t ldx, int8_t* __restrict__ Qt, int64_t ldqt,
+                                               float* __restrict__ scale, int vec_in, int vec_out,
+                                               int bid, int nbands, char* smem) {
   constexpr int C4 = BC / 4;                 // threads per row
   constexpr int RPP = QCR_THREADS / C4;      // rows per pass
-  constexpr int TILE = QCR_MAX_ELEMS;        // bytes of the transposed tile
-  __shared__ float red[QCR_THREADS / 64][BC];
-  __shared__ float s_inv[BC];
-  __shared__ __attribute__((aligned(16))) int8_t tile[TILE];
+  int8_t* tile = reinterpret_cast<int8_t*>(smem);
+  float (*red)[BC] = reinterpret_cast<float (*)[BC]>(smem + QCR_MAX_ELEMS);
+  float* s_inv = reinterpret_cast<float*>(smem + QCR_MAX_ELEMS + (QCR_THREADS / 64) * BC * 4);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t j0 = (int64_t)xcd_grouped(blockIdx.x, gridDim.x) * BC;
+  const int64_t j0 = (int64_t)xcd_grouped(bid, nbands) * BC;
   const int cg = tid % C4, r_off = tid / C4;
   const int rp = (int)((rows + 15) / 16 * 16);     // tile row pitch (bytes per column)
 
@@ -394,6 +430,16 @@ qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_
       for (int e = 0; e < 16 && off + e < rows; ++e) dst[e] = src[e];
     }
   }
+}
+
+template <int BC, int FMT>
+__global__ void __launch_bounds__(QCR_THREADS)
+qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                 int8_t* __restrict__ Qt, int64_t ldqt, float* __restrict__ scale, int vec_in,
+                 int vec_out) {
+  __shared__ __attribute__((aligned(16))) char smem[QCR_SMEM_BYTES];
+  qcols_reg_body<BC, FMT>(X, rows, cols, ldx, Qt, ldqt, scale, vec_in, vec_out, blockIdx.x, gridDim.x,
+                          smem);
 }
 
 // Band width for the one-kernel path: as wide as the registers allow (BC *
@@ -567,6 +613,95 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
     case FMT_INT4: return quantize_cols_int4<FMT_INT4>(X, rows, cols, ldx, Qt, ldqt, scale, stream);
     default: return quantize_cols_int4<FMT_INT4 | FMT_POW2>(X, rows, cols, ldx, Qt, ldqt, scale, stream);
   }
+}
+
+
+// ---------------------------------------------------------------------------
+// quantize_batch: independent int8 row / column passes in one launch of
+// 1024-thread workgroups.  Each job owns a range of workgroup ids, rounded up
+// to a multiple of 8 so that an id keeps its XCD (ids are dealt to the 8 XCDs
+// round-robin) within the range; a workgroup finds its job by scanning the
+// range starts (uniform across the workgroup) and runs the job's kernel body
+// with its index inside the range.  Small passes, bound by latency alone,
+// then share the chip instead of following one another.
+// ---------------------------------------------------------------------------
+enum QKind : int { QK_ROWS_WAVE = 0, QK_ROWS_BLOCK = 1, QK_COLS_REG = 2 };
+
+template <int FMT>
+__device__ __forceinline__ void run_qjob(const QJob& q, int bid, char* smem) {
+  if (q.kind == QK_ROWS_WAVE) {
+    switch (q.param) {
+      case 1: qrows_wave_body<1, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
+      case 2: qrows_wave_body<2, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
+      case 3: qrows_wave_body<3, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
+      default: qrows_wave_body<4, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
+    }
+  } else {
+    switch (q.param) {
+      case 64: qcols_reg_body<64, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      case 32: qcols_reg_body<32, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      case 16: qcols_reg_body<16, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      case 8: qcols_reg_body<8, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      default: qcols_reg_body<4, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(1024) quantize_batch_kernel(const QBatch b) {
+  __shared__ __attribute__((aligned(16))) char smem[QCR_SMEM_BYTES];
+  const int id = blockIdx.x;
+  int j = 0;
+  while (j + 1 < b.n && id >= b.job[j + 1].first) ++j;
+  const QJob& q = b.job[j];
+  const int bid = id - q.first;
+  if (bid >= q.blocks) return;   // the padding of the job's range
+  if (q.fmt & FMT_POW2)
+    run_qjob<FMT_POW2>(q, bid, smem);
+  else
+    run_qjob<0>(q, bid, smem);
+}
+
+bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
+               float* scale, bool by_col, int fmt, QJob& q) {
+  if ((fmt & FMT_INT4) || rows <= 0 || cols <= 0) return false;
+  q.X = X; q.Q = Q; q.scale = scale;
+  q.rows = rows; q.cols = cols; q.ldx = ldx; q.ldq = ldq;
+  q.fmt = fmt;
+  q.vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
+  if (!by_col) {
+    q.vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
+    // only short rows (at most 1024 values, 4 float4 per lane): the kernel's
+    // registers are the largest of its bodies', and longer rows would halve
+    // the workgroups a CU holds for every job of the launch
+    const int vpl = rows_wave_vpl(cols);
+    if (vpl == 0 || vpl > 4) return false;
+    q.kind = QK_ROWS_WAVE; q.param = vpl;
+    q.blocks = (int)((rows + 15) / 16);   // 16 waves per workgroup, a wave per row
+    return true;
+  }
+  q.vec_out = ((uintptr_t)Q % 16 == 0) && (ldq % 16 == 0);
+  const int bc = qcols_band(rows, cols);
+  const char* force = getenv("I8G_QCOLS_TWO_PASS");
+  if (bc == 0 || (force && force[0] == '1')) return false;   // the multi-kernel path
+  q.kind = QK_COLS_REG; q.param = bc;
+  q.blocks = (int)((cols + bc - 1) / bc);
+  return true;
+}
+
+hipError_t launch_quantize_batch(QJob* jobs, int n, hipStream_t stream) {
+  for (int i0 = 0; i0 < n; i0 += kQBatchMax) {
+    QBatch b;
+    b.n = n - i0 < kQBatchMax ? n - i0 : kQBatchMax;
+    int64_t next = 0;
+    for (int j = 0; j < b.n; ++j) {
+      b.job[j] = jobs[i0 + j];
+      b.job[j].first = (int)next;
+      next += (b.job[j].blocks + 7) / 8 * 8;
+    }
+    if (next > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_batch_kernel, dim3((unsigned int)next), dim3(1024), 0, stream, b);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace i8g
