@@ -277,8 +277,11 @@ typedef struct i8g_gate_report {
                         5 the gate's inputs separate no wrong specification
                         (index = which one: 0 round-half-even quantize,
                         1 fused multiply-add quantize, 2 column scale first,
-                        3 scales multiplied first, 4 ReLU's +0)            */
-  int32_t config;    /* GEMM tile configuration that failed, or -1         */
+                        3 scales multiplied first, 4 ReLU's +0),
+                        6 GEMM output with int4 operands,
+                        7 gemm_i8_requant codes or scales                  */
+  int32_t config;    /* GEMM tile configuration that failed (for checks 1
+                        and 2 the storage format), or -1                    */
   int64_t m, n, k;   /* shape of the failing case (rows, cols for quantize) */
   int64_t index;     /* first differing element (row-major), line, or -1   */
   uint32_t got, want;/* bit patterns at that element (low 32 bits of a hash) */
@@ -290,10 +293,12 @@ size_t i8g_gate_workspace_bytes(void);
 
 /*
  * i8g_gate -- init gate: runs quantize_rows and quantize_cols (row and
- * column passes, a long row, a tall column pass), the GEMM in every tile
- * configuration of the planner (ReLU on and off, a split K) and the fused
- * and standalone output hash on ragged shapes, and compares every output bit
- * with an exact host mirror of the method built into the library.  The
+ * column passes, a long row, a tall column pass, the pow2 and int4 formats,
+ * quantize_batch), the GEMM in every tile configuration of the planner
+ * (ReLU on and off, a split K), the GEMM with int4 operands,
+ * gemm_i8_requant, and the fused and standalone output hash on ragged
+ * shapes, and compares every output bit with an exact host mirror of the
+ * method built into the library.  The
  * inputs hold exact ties x*inv = k + 0.5 and products just below 0.5 (where
  * round-half-even and a fused multiply-add quantize differ from the method),
  * and the gate checks that its GEMM outputs also separate the method from a

@@ -86,6 +86,39 @@ static void quantize_line(const float* x, int64_t n, int64_t stride, int8_t* q, 
   const float inv = 1.0f / *s;
   for (int64_t k = 0; k < n; ++k) q[k] = (int8_t)quant(x[k * stride], inv);
 }
+// Storage formats (the presk page, section "Integer weights"): qmax 7 for
+// int4, the scale rounded up to a power of two for pow2.
+static inline float scale_of_fmt(float a, int fmt) {
+  const float s0 = a / ((fmt & FMT_INT4) ? 7.0f : 127.0f);
+  const float fl = from_bits(0x322BCC77u);
+  float s = s0 > fl ? s0 : fl;
+  if (fmt & FMT_POW2) {
+    int e = 0;
+    const float m = frexpf(s, &e);   // s = m * 2^e, m in [0.5, 1)
+    s = ldexpf(1.0f, m == 0.5f ? e - 1 : e);
+  }
+  return s;
+}
+static void quantize_line_fmt(const float* x, int64_t n, int64_t stride, int8_t* q, float* s, int fmt) {
+  float a = 0.0f;
+  for (int64_t k = 0; k < n; ++k) {
+    const float v = fabsf(x[k * stride]);
+    a = v > a ? v : a;
+  }
+  *s = scale_of_fmt(a, fmt);
+  const float inv = 1.0f / *s;
+  for (int64_t k = 0; k < n; ++k) q[k] = (int8_t)quant(x[k * stride], inv);
+}
+// int4 line layout: value k in byte 16*(k/32) + k%16, low nibble when
+// k%32 < 16, else high; 16*ceil(n/32) bytes, unused nibbles 0.
+static void pack_int4(const int8_t* q, int64_t n, uint8_t* out) {
+  const int64_t bytes = (n + 31) / 32 * 16;
+  for (int64_t b = 0; b < bytes; ++b) out[b] = 0;
+  for (int64_t k = 0; k < n; ++k) {
+    const int64_t b = 16 * (k / 32) + k % 16;
+    out[b] |= (uint8_t)(((unsigned)q[k] & 0xFu) << ((k % 32) < 16 ? 0 : 4));
+  }
+}
 static float epilogue(int32_t acc, float sr, float sc, bool relu) {
   float y = (float)acc;
   y = y * sr;
@@ -229,10 +262,16 @@ inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // ---------------------------------------------------------------------------
 // the gate
 // ---------------------------------------------------------------------------
-struct QCase { int64_t rows, cols; bool by_col; };
+struct QCase { int64_t rows, cols; bool by_col; int fmt; bool batch; };
 struct GCase { int64_t M, N, K; int splits; };
-const QCase kQCases[] = {{37, 301, false}, {5, 4500, false}, {1, 1, false}, {300, 37, true},
-                         {8200, 33, true}, {700, 64, true}};
+// the last four int8 cases run as quantize_batch calls (with a second job)
+const QCase kQCases[] = {{37, 301, false, 0, false},  {5, 4500, false, 0, false},
+                         {1, 1, false, 0, false},     {300, 37, true, 0, false},
+                         {8200, 33, true, 0, false},  {700, 64, true, 0, false},
+                         {37, 301, false, FMT_INT4, false},  {300, 37, true, FMT_INT4 | FMT_POW2, false},
+                         {64, 100, false, FMT_POW2, false},  {100, 64, true, FMT_POW2, false},
+                         {65, 1000, false, 0, true},  {1000, 65, true, 0, true},
+                         {33, 700, false, FMT_POW2, true}, {700, 33, true, 0, true}};
 const GCase kGCases[] = {{17, 33, 15, 0}, {130, 190, 70, 0}, {300, 520, 192, 0},
                          {256, 200, 768, 0}, {64, 64, 4096, 4}};
 constexpr int kGateCfgs = 7;   // tile configurations of the GEMM planner
@@ -300,7 +339,7 @@ int gate_quantize(GateRun& g, const QCase& c, int case_id, int64_t counts[2]) {
   std::vector<float> Sw(nlines);
   for (int64_t l = 0; l < nlines; ++l) {
     const float* base = c.by_col ? &X[l] : &X[l * Cc];
-    mirror::quantize_line(base, len, c.by_col ? Cc : 1, &Qw[l * len], &Sw[l]);
+    mirror::quantize_line_fmt(base, len, c.by_col ? Cc : 1, &Qw[l * len], &Sw[l], c.fmt);
     const float inv = 1.0f / Sw[l];
     for (int64_t e = 0; e < len; ++e) {
       const float x = base[e * (c.by_col ? Cc : 1)];
@@ -309,16 +348,29 @@ int gate_quantize(GateRun& g, const QCase& c, int case_id, int64_t counts[2]) {
       if ((int)floorf(fmaf(x, inv, 0.5f)) != q) ++counts[1];        // fused multiply-add
     }
   }
-  // the device
+  // the device (int4: lines of whole 16-byte groups; a batch adds the
+  // other direction of the same X as a second job, which must not disturb it)
+  const bool int4 = (c.fmt & FMT_INT4) != 0;
   g.cursor = 256;
   float* dX = reinterpret_cast<float*>(g.take(n * 4));
-  const int64_t ldq = len;
+  const int64_t ldq = int4 ? (len + 31) / 32 * 16 : len;
   int8_t* dQ = reinterpret_cast<int8_t*>(g.take(nlines * ldq + 16));
   float* dS = reinterpret_cast<float*>(g.take(nlines * 4));
+  const int64_t olines = c.by_col ? R : Cc, olen = c.by_col ? Cc : R;
+  int8_t* dQ2 = reinterpret_cast<int8_t*>(g.take(olines * olen + 16));
+  float* dS2 = reinterpret_cast<float*>(g.take(olines * 4));
   if (g.cursor > kGateWorkspace) return I8G_EWORKSPACE;
   int st = hipok(hipMemcpyAsync(dX, X.data(), n * 4, hipMemcpyHostToDevice, g.st));
   if (st) return st;
-  st = c.by_col ? quantize_cols(dX, R, Cc, Cc, dQ, ldq, dS, g.st) : quantize_rows(dX, R, Cc, Cc, dQ, ldq, dS, g.st);
+  if (c.batch) {
+    i8g_quantize_job jobs[2] = {
+        {dX, R, Cc, Cc, dQ, ldq, dS, c.by_col ? 1u : 0u, (uint32_t)c.fmt},
+        {dX, R, Cc, Cc, dQ2, olen, dS2, c.by_col ? 0u : 1u, 0u}};
+    st = quantize_batch(jobs, 2, g.st);
+  } else {
+    st = c.by_col ? quantize_cols_fmt(dX, R, Cc, Cc, dQ, ldq, dS, (uint32_t)c.fmt, g.st)
+                  : quantize_rows_fmt(dX, R, Cc, Cc, dQ, ldq, dS, (uint32_t)c.fmt, g.st);
+  }
   if (st) return st;
   std::vector<int8_t> Qg(nlines * ldq);
   std::vector<float> Sg(nlines);
@@ -327,12 +379,38 @@ int gate_quantize(GateRun& g, const QCase& c, int case_id, int64_t counts[2]) {
   if (!st) st = hipok(hipStreamSynchronize(g.st));
   if (st) return st;
   const int check = c.by_col ? 2 : 1;
+  std::vector<uint8_t> packed(ldq);
   for (int64_t l = 0; l < nlines; ++l) {
     if (mirror::to_bits(Sg[l]) != mirror::to_bits(Sw[l]))
-      return fail(g.rep, check, -1, R, Cc, 0, l, mirror::to_bits(Sg[l]), mirror::to_bits(Sw[l]));
+      return fail(g.rep, check, c.fmt, R, Cc, 0, l, mirror::to_bits(Sg[l]), mirror::to_bits(Sw[l]));
+    if (int4) {
+      mirror::pack_int4(&Qw[l * len], len, packed.data());
+      for (int64_t b = 0; b < ldq; ++b)
+        if ((uint8_t)Qg[l * ldq + b] != packed[b])
+          return fail(g.rep, check, c.fmt, R, Cc, 0, l * ldq + b, (uint8_t)Qg[l * ldq + b], packed[b]);
+      continue;
+    }
     for (int64_t e = 0; e < len; ++e)
       if (Qg[l * ldq + e] != Qw[l * len + e])
-        return fail(g.rep, check, -1, R, Cc, 0, l * len + e, (uint8_t)Qg[l * ldq + e], (uint8_t)Qw[l * len + e]);
+        return fail(g.rep, check, c.fmt, R, Cc, 0, l * len + e, (uint8_t)Qg[l * ldq + e], (uint8_t)Qw[l * len + e]);
+  }
+  if (c.batch) {   // the second job: int8, the other direction
+    std::vector<int8_t> Q2(olines * olen), Q2w(olen);
+    std::vector<float> S2(olines);
+    st = hipok(hipMemcpyAsync(Q2.data(), dQ2, olines * olen, hipMemcpyDeviceToHost, g.st));
+    if (!st) st = hipok(hipMemcpyAsync(S2.data(), dS2, olines * 4, hipMemcpyDeviceToHost, g.st));
+    if (!st) st = hipok(hipStreamSynchronize(g.st));
+    if (st) return st;
+    for (int64_t l = 0; l < olines; ++l) {
+      float sw = 0.0f;
+      const float* base = c.by_col ? &X[l * Cc] : &X[l];
+      mirror::quantize_line_fmt(base, olen, c.by_col ? 1 : Cc, Q2w.data(), &sw, 0);
+      if (mirror::to_bits(S2[l]) != mirror::to_bits(sw))
+        return fail(g.rep, c.by_col ? 1 : 2, 0, R, Cc, 0, l, mirror::to_bits(S2[l]), mirror::to_bits(sw));
+      for (int64_t e = 0; e < olen; ++e)
+        if (Q2[l * olen + e] != Q2w[e])
+          return fail(g.rep, c.by_col ? 1 : 2, 0, R, Cc, 0, l * olen + e, (uint8_t)Q2[l * olen + e], (uint8_t)Q2w[e]);
+    }
   }
   return I8G_OK;
 }
@@ -416,6 +494,138 @@ int gate_gemm(GateRun& g, const GCase& c, int case_id, int64_t counts[3], int* n
   return I8G_OK;
 }
 
+// int4 operands: the mirror quantizes A and/or B with qmax 7 (B with
+// power-of-two scales) and packs the codes; the device runs the GEMM on the
+// packed bytes.  The expected output is the mirror's exact contraction of
+// the codes and its epilogue.
+struct G4Case { int64_t M, N, K; bool a4, b4; };
+const G4Case kG4Cases[] = {{130, 190, 70, false, true}, {256, 200, 768, true, false}, {65, 33, 1000, true, true}};
+
+int upload_operand(GateRun& g, const std::vector<int8_t>& codes, int64_t rows, int64_t K, bool int4,
+                   int64_t* ld_out, int8_t** dptr) {
+  const int64_t ld = int4 ? (K + 31) / 32 * 16 : round16(K);
+  std::vector<uint8_t> buf(rows * ld, 0);
+  for (int64_t r = 0; r < rows; ++r) {
+    if (int4) mirror::pack_int4(&codes[r * K], K, &buf[r * ld]);
+    else memcpy(&buf[r * ld], &codes[r * K], K);
+  }
+  *dptr = reinterpret_cast<int8_t*>(g.take(rows * ld));
+  *ld_out = ld;
+  return hipok(hipMemcpyAsync(*dptr, buf.data(), rows * ld, hipMemcpyHostToDevice, g.st));
+}
+
+int gate_gemm_int4(GateRun& g, const G4Case& c, int case_id, int* ncases) {
+  const int64_t M = c.M, N = c.N, K = c.K;
+  const bool relu = (case_id & 1) != 0;
+  const int fa = c.a4 ? FMT_INT4 : 0, fb = c.b4 ? (FMT_INT4 | FMT_POW2) : FMT_POW2;
+  std::vector<float> A(M * K), B(N * K);
+  for (int64_t e = 0; e < M * K; ++e) A[e] = mirror::gate_value(0x6E4A0000ull + case_id, e);
+  for (int64_t e = 0; e < N * K; ++e) B[e] = mirror::gate_value(0x6E4B0000ull + case_id, e);
+  std::vector<int8_t> QA(M * K), QB(N * K);
+  std::vector<float> sr(M), sc(N);
+  for (int64_t i = 0; i < M; ++i) mirror::quantize_line_fmt(&A[i * K], K, 1, &QA[i * K], &sr[i], fa);
+  for (int64_t j = 0; j < N; ++j) mirror::quantize_line_fmt(&B[j * K], K, 1, &QB[j * K], &sc[j], fb);
+  std::vector<float> Cw(M * N);
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < N; ++j) {
+      int32_t t = 0;
+      for (int64_t k = 0; k < K; ++k) t += (int32_t)QA[i * K + k] * (int32_t)QB[j * K + k];
+      Cw[i * N + j] = mirror::epilogue(t, sr[i], sc[j], relu);
+    }
+  const uint64_t Hw = mirror::hash_of(Cw.data(), M, N);
+  g.cursor = 256;
+  int8_t *dA = nullptr, *dB = nullptr;
+  int64_t lda = 0, ldb = 0;
+  int st = upload_operand(g, QA, M, K, c.a4, &lda, &dA);
+  if (!st) st = upload_operand(g, QB, N, K, c.b4, &ldb, &dB);
+  float* dsr = reinterpret_cast<float*>(g.take(M * 4));
+  float* dsc = reinterpret_cast<float*>(g.take(N * 4));
+  float* dC = reinterpret_cast<float*>(g.take(M * N * 4));
+  uint64_t* dH = reinterpret_cast<uint64_t*>(g.take(16));
+  const GemmPlan plan = plan_gemm_int4(M, N, K, -1);
+  char* gw = g.take(plan.workspace_bytes);
+  if (g.cursor > kGateWorkspace) return I8G_EWORKSPACE;
+  if (!st) st = hipok(hipMemcpyAsync(dsr, sr.data(), M * 4, hipMemcpyHostToDevice, g.st));
+  if (!st) st = hipok(hipMemcpyAsync(dsc, sc.data(), N * 4, hipMemcpyHostToDevice, g.st));
+  if (st) return st;
+  hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(64), 0, g.st, reinterpret_cast<unsigned int*>(gw));
+  const uint32_t flags = (relu ? I8G_RELU : 0u) | I8G_HASH | (c.a4 ? I8G_A_INT4 : 0u) | (c.b4 ? I8G_B_INT4 : 0u);
+  st = enqueue_gemm(dA, lda, dsr, dB, ldb, dsc, M, N, K, dC, N, flags, dH, gw, plan.workspace_bytes, g.st, -2, 0);
+  if (st) return st;
+  std::vector<float> Cg(M * N);
+  uint64_t Hg = 0;
+  st = hipok(hipMemcpyAsync(Cg.data(), dC, M * N * 4, hipMemcpyDeviceToHost, g.st));
+  if (!st) st = hipok(hipMemcpyAsync(&Hg, dH, 8, hipMemcpyDeviceToHost, g.st));
+  if (!st) st = hipok(hipStreamSynchronize(g.st));
+  if (st) return st;
+  for (int64_t e = 0; e < M * N; ++e)
+    if (mirror::to_bits(Cg[e]) != mirror::to_bits(Cw[e]))
+      return fail(g.rep, 6, plan.cfg, M, N, K, e, mirror::to_bits(Cg[e]), mirror::to_bits(Cw[e]));
+  if (Hg != Hw) return fail(g.rep, 4, plan.cfg, M, N, K, -1, (uint32_t)Hg, (uint32_t)Hw);
+  ++*ncases;
+  return I8G_OK;
+}
+
+// The requantizing epilogue: codes and scales must be the mirror's per-row
+// quantization of the mirror's output, and the hash that output's hash.
+int gate_requant(GateRun& g, int* ncases) {
+  const int64_t M = 300, N = 520, K = 192, ld = round16(K);
+  std::vector<float> A(M * K), B(N * K);
+  for (int64_t e = 0; e < M * K; ++e) A[e] = mirror::gate_value(0x6E5A0000ull, e);
+  for (int64_t e = 0; e < N * K; ++e) B[e] = mirror::gate_value(0x6E5B0000ull, e);
+  std::vector<int8_t> QA(M * K), QB(N * K);
+  std::vector<float> sr(M), sc(N);
+  for (int64_t i = 0; i < M; ++i) mirror::quantize_line_fmt(&A[i * K], K, 1, &QA[i * K], &sr[i], 0);
+  for (int64_t j = 0; j < N; ++j) mirror::quantize_line_fmt(&B[j * K], K, 1, &QB[j * K], &sc[j], 0);
+  std::vector<float> Cw(M * N);
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < N; ++j) {
+      int32_t t = 0;
+      for (int64_t k = 0; k < K; ++k) t += (int32_t)QA[i * K + k] * (int32_t)QB[j * K + k];
+      Cw[i * N + j] = mirror::epilogue(t, sr[i], sc[j], true);
+    }
+  std::vector<int8_t> Qw(M * N);
+  std::vector<float> Sw(M);
+  for (int64_t i = 0; i < M; ++i) mirror::quantize_line_fmt(&Cw[i * N], N, 1, &Qw[i * N], &Sw[i], 0);
+  const uint64_t Hw = mirror::hash_of(Cw.data(), M, N);
+  g.cursor = 256;
+  int8_t *dA = nullptr, *dB = nullptr;
+  int64_t lda = 0, ldb = 0;
+  int st = upload_operand(g, QA, M, K, false, &lda, &dA);
+  if (!st) st = upload_operand(g, QB, N, K, false, &ldb, &dB);
+  float* dsr = reinterpret_cast<float*>(g.take(M * 4));
+  float* dsc = reinterpret_cast<float*>(g.take(N * 4));
+  int8_t* dQ = reinterpret_cast<int8_t*>(g.take(M * N));
+  float* dS = reinterpret_cast<float*>(g.take(M * 4));
+  uint64_t* dH = reinterpret_cast<uint64_t*>(g.take(16));
+  const size_t wsb = gemm_i8_requant_workspace_bytes(M, N, K);
+  char* gw = g.take(wsb);
+  if (g.cursor > kGateWorkspace) return I8G_EWORKSPACE;
+  (void)ld;
+  if (!st) st = hipok(hipMemcpyAsync(dsr, sr.data(), M * 4, hipMemcpyHostToDevice, g.st));
+  if (!st) st = hipok(hipMemcpyAsync(dsc, sc.data(), N * 4, hipMemcpyHostToDevice, g.st));
+  if (st) return st;
+  hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(64), 0, g.st, reinterpret_cast<unsigned int*>(gw));
+  st = gemm_i8_requant(dA, lda, dsr, dB, ldb, dsc, M, N, K, dQ, N, dS, I8G_RELU | I8G_HASH, dH, gw, wsb, g.st);
+  if (st) return st;
+  std::vector<int8_t> Qg(M * N);
+  std::vector<float> Sg(M);
+  uint64_t Hg = 0;
+  st = hipok(hipMemcpyAsync(Qg.data(), dQ, M * N, hipMemcpyDeviceToHost, g.st));
+  if (!st) st = hipok(hipMemcpyAsync(Sg.data(), dS, M * 4, hipMemcpyDeviceToHost, g.st));
+  if (!st) st = hipok(hipMemcpyAsync(&Hg, dH, 8, hipMemcpyDeviceToHost, g.st));
+  if (!st) st = hipok(hipStreamSynchronize(g.st));
+  if (st) return st;
+  for (int64_t i = 0; i < M; ++i)
+    if (mirror::to_bits(Sg[i]) != mirror::to_bits(Sw[i]))
+      return fail(g.rep, 7, -1, M, N, K, i, mirror::to_bits(Sg[i]), mirror::to_bits(Sw[i]));
+  for (int64_t e = 0; e < M * N; ++e)
+    if (Qg[e] != Qw[e]) return fail(g.rep, 7, -1, M, N, K, e, (uint8_t)Qg[e], (uint8_t)Qw[e]);
+  if (Hg != Hw) return fail(g.rep, 4, -1, M, N, K, -1, (uint32_t)Hg, (uint32_t)Hw);
+  ++*ncases;
+  return I8G_OK;
+}
+
 }  // namespace
 }  // namespace i8g
 
@@ -441,6 +651,15 @@ int i8g_gate(void* workspace, size_t workspace_bytes, void* stream, i8g_gate_rep
   id = 0;
   for (const GCase& c : kGCases) {
     const int st = gate_gemm(g, c, id++, gcounts, &cases);
+    if (st) return st;
+  }
+  id = 0;
+  for (const G4Case& c : kG4Cases) {
+    const int st = gate_gemm_int4(g, c, id++, &cases);
+    if (st) return st;
+  }
+  {
+    const int st = gate_requant(g, &cases);
     if (st) return st;
   }
   if (report) report->cases = cases;

@@ -26,7 +26,8 @@ def test_gate_passes(g):
     rc, rep = g.gate()
     assert rc == 0, (g.load().i8g_status_string(rc), rep)
     assert rep["check"] == 0
-    assert rep["cases"] >= 6 + 5 * 7          # quantize cases + GEMM cases x configurations
+    # quantize cases (14) + GEMM cases x configurations (5 x 7) + int4 GEMMs (3) + requant (1)
+    assert rep["cases"] >= 14 + 5 * 7 + 3 + 1
 
 
 def _live_gemm(g, M, N, K, relu, seed):
