@@ -137,7 +137,7 @@ class GpuStep:
                      C=torch.empty((M, N), dtype=torch.float32, device=dev),
                      h=torch.zeros(1, dtype=torch.int64, device=dev), ld=ld)
             self.t[e["out"]] = e["C"]
-            ws_bytes = max(ws_bytes, g.workspace_bytes(M, N, K))
+            ws_bytes = max(ws_bytes, g.workspace_bytes(M, N, K, 8 if fmt_b & 2 else 0))
             self.gemms.append(e)
         # requantizing epilogue: a GEMM whose output is the per-row quantized A
         # operand of a later GEMM writes that GEMM's codes and scales itself

@@ -174,8 +174,9 @@ int quantize_batch(const i8g_quantize_job* jobs, int32_t n, void* stream);
  *   C      M x N f32 output, row-major, leading dimension ldc >= N.
  *   flags  I8G_RELU and/or I8G_HASH; I8G_A_INT4 / I8G_B_INT4 when QA / QBt
  *          hold int4 values in the layout of quantize_rows_fmt (then that
- *          operand's ld need only cover 16*ceil(K/32) bytes).  Scales of
- *          either scheme are taken as they are.
+ *          operand's ld need only cover 16*ceil(K/32) bytes; the
+ *          workspace must then be gemm_i8_workspace_bytes_flags(M, N, K,
+ *          flags) bytes).  Scales of either scheme are taken as they are.
  *   hash   device pointer to one uint64_t, required with I8G_HASH (else
  *          ignored): receives output_hash(C) for this output.
  *   workspace, workspace_bytes
@@ -202,8 +203,13 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row,
                         float* C, int64_t ldc, uint32_t flags, uint64_t* hash,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256). */
+/* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256),
+ * for int8 operands. */
 size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+/* The same for the given flags: with I8G_A_INT4 / I8G_B_INT4 the workspace
+ * also holds the int4 operands widened to int8 (the int8 kernels then run
+ * the product), 32*ceil(K/32) bytes per row of each such operand. */
+size_t gemm_i8_workspace_bytes_flags(int64_t M, int64_t N, int64_t K, uint32_t flags);
 
 /*
  * gemm_i8_requant -- the requantizing epilogue: the GEMM's output leaves as

@@ -41,7 +41,8 @@ EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_wo
             "output_hash", "output_hash_workspace_bytes", "i8g_status_string", "i8g_version",
             "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
             "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt",
-            "gemm_i8_requant", "gemm_i8_requant_workspace_bytes", "quantize_batch")
+            "gemm_i8_requant", "gemm_i8_requant_workspace_bytes", "quantize_batch",
+            "gemm_i8_workspace_bytes_flags")
 
 _lib = None
 _ws = {}
@@ -85,6 +86,8 @@ def load():
     lib.gemm_i8_requant.restype = ctypes.c_int
     lib.gemm_i8_requant_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
     lib.gemm_i8_requant_workspace_bytes.restype = c_sz
+    lib.gemm_i8_workspace_bytes_flags.argtypes = [c_i64, c_i64, c_i64, c_u32]
+    lib.gemm_i8_workspace_bytes_flags.restype = c_sz
     lib.gemm_i8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
     lib.gemm_i8_workspace_bytes.restype = c_sz
     lib.output_hash.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
@@ -242,8 +245,8 @@ def quantize_batch(specs):
     return outs
 
 
-def workspace_bytes(M, N, K):
-    return int(load().gemm_i8_workspace_bytes(M, N, K))
+def workspace_bytes(M, N, K, flags=0):
+    return int(load().gemm_i8_workspace_bytes_flags(M, N, K, flags))
 
 
 def _workspace(device, nbytes):
@@ -283,10 +286,9 @@ def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=
     C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
     _req_matrix(C, torch.float32, "out")
     h = torch.zeros(1, dtype=torch.int64, device=dev) if want_hash else None
-    nbytes = workspace_bytes(M, N, K)
-    ws = _workspace(dev, nbytes)
     flags = ((I8G_RELU if relu else 0) | (I8G_HASH if want_hash else 0) |
              (I8G_A_INT4 if a_int4 else 0) | (I8G_B_INT4 if b_int4 else 0))
+    ws = _workspace(dev, workspace_bytes(M, N, K, flags))
     lda = QA.stride(0) if M > 0 else _round16(K)
     ldb = QBt.stride(0) if N > 0 else _round16(K)
     _check(load().gemm_i8_blockscaled(

@@ -47,12 +47,38 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
       return I8G_EALIGN;
   }
   // force_tile == -2: the library's own choice (plan_gemm, which honours the
-  // test overrides); otherwise exactly the forced configuration
-  GemmPlan plan = (a4 || b4) ? plan_gemm_int4(M, N, K > 0 ? K : 1, force_tile == -2 ? -1 : force_splits)
-                  : force_tile == -2
+  // test overrides); -3: the direct int4 kernel; otherwise exactly the forced
+  // configuration
+  const bool direct4 = (a4 || b4) && (force_tile == -3 || (force_tile == -2 && int4_direct_requested()));
+  GemmPlan plan = direct4 ? plan_gemm_int4(M, N, K > 0 ? K : 1, force_tile < 0 ? -1 : force_splits)
+                  : force_tile < 0
                       ? plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc)
                       : plan_gemm_forced(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc, force_tile, force_splits);
   if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
+  bool wa = false, wb = false;   // operands widened into the workspace
+  if ((a4 || b4) && !direct4 && K > 0) {
+    const int64_t ldw = int4_widened_ld(K);
+    size_t off = (plan.workspace_bytes + 255) / 256 * 256;
+    const size_t need = off + (a4 ? ((size_t)M * ldw + 255) / 256 * 256 : 0) +
+                        (b4 ? ((size_t)N * ldw + 255) / 256 * 256 : 0);
+    if (workspace_bytes < need) return I8G_EWORKSPACE;
+    char* ws = reinterpret_cast<char*>(workspace);
+    if (a4) {
+      int8_t* w = reinterpret_cast<int8_t*>(ws + off);
+      if (launch_widen_int4(QA, lda, M, K, w, stream) != hipSuccess) return I8G_EHIP;
+      QA = w;
+      lda = ldw;
+      off += ((size_t)M * ldw + 255) / 256 * 256;
+      wa = true;
+    }
+    if (b4) {
+      int8_t* w = reinterpret_cast<int8_t*>(ws + off);
+      if (launch_widen_int4(QBt, ldb, N, K, w, stream) != hipSuccess) return I8G_EHIP;
+      QBt = w;
+      ldb = ldw;
+      wb = true;
+    }
+  }
   GemmParams p;
   p.A = QA;
   p.B = QBt;
@@ -79,8 +105,8 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
   p.partials = reinterpret_cast<int*>(ws + plan.partials_offset);
   p.comb_rows = plan.comb_rows;
   p.hash_out = hash;
-  p.a4 = a4 ? 1 : 0;
-  p.b4 = b4 ? 1 : 0;
+  p.a4 = (a4 && !wa) ? 1 : 0;
+  p.b4 = (b4 && !wb) ? 1 : 0;
   return hip_status(launch_gemm(p, plan, stream));
 }
 
@@ -181,16 +207,26 @@ int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_
   return quantize_cols_fmt(X, rows, cols, ldx, Qt, ldqt, scale, 0u, stream);
 }
 
-size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+size_t gemm_i8_workspace_bytes_flags(int64_t M, int64_t N, int64_t K, uint32_t flags) {
   if (M <= 0 || N <= 0) return 256;
   // the plan may depend on ldc (very wide rows exclude the persistent
   // kernel): size for either
   const GemmPlan a = plan_gemm(M, N, K > 0 ? K : 1, true);
   const GemmPlan b = plan_gemm(M, N, K > 0 ? K : 1, false);
-  const GemmPlan c = plan_gemm_int4(M, N, K > 0 ? K : 1, -1);   // int4 operands
   size_t bytes = a.workspace_bytes > b.workspace_bytes ? a.workspace_bytes : b.workspace_bytes;
-  bytes = bytes > c.workspace_bytes ? bytes : c.workspace_bytes;
+  if (flags & (I8G_A_INT4 | I8G_B_INT4)) {
+    const GemmPlan c = plan_gemm_int4(M, N, K > 0 ? K : 1, -1);   // the direct int4 kernel
+    const int64_t ldw = int4_widened_ld(K > 0 ? K : 1);
+    const size_t widened = (bytes + 255) / 256 * 256 +
+                           ((flags & I8G_A_INT4) ? ((size_t)M * ldw + 255) / 256 * 256 : 0) +
+                           ((flags & I8G_B_INT4) ? ((size_t)N * ldw + 255) / 256 * 256 : 0);
+    bytes = widened > c.workspace_bytes ? widened : c.workspace_bytes;
+  }
   return bytes > 256 ? bytes : 256;
+}
+
+size_t gemm_i8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return gemm_i8_workspace_bytes_flags(M, N, K, 0u);
 }
 
 size_t output_hash_workspace_bytes(void) { return kWsHeader + (size_t)kHashMaxParts * 8; }

@@ -2103,4 +2103,50 @@ hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, hipStream_t s
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// int4 operand widened to int8 codes (the value q itself) in rows of
+// int4_widened_ld(K) bytes, so that the int8 kernels (and their planner) run
+// the GEMM: one thread per 16-byte packed group.  A nibble n becomes the
+// byte n | (bit 3 of n) * 0xF0, its sign extension.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned int sext_nibble_bytes(unsigned int n) {
+  return n | (((n >> 3) & 0x01010101u) * 0xF0u);
+}
+
+__global__ void __launch_bounds__(256)
+widen_int4_kernel(const int8_t* __restrict__ P, int64_t ldp, int64_t rows, int64_t groups,
+                  int8_t* __restrict__ Q, int64_t ldq) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * groups) return;
+  const int64_t r = t / groups, gi = t % groups;
+  const v4i w = *reinterpret_cast<const v4i*>(P + r * ldp + gi * 16);
+  v4i lo, hi;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = (int)sext_nibble_bytes((unsigned int)w[e] & 0x0F0F0F0Fu);
+    hi[e] = (int)sext_nibble_bytes(((unsigned int)w[e] >> 4) & 0x0F0F0F0Fu);
+  }
+  int8_t* q = Q + r * ldq + gi * 32;
+  *reinterpret_cast<v4i*>(q) = lo;
+  *reinterpret_cast<v4i*>(q + 16) = hi;
+}
+
+int64_t int4_widened_ld(int64_t K) { return (K + 31) / 32 * 32; }
+
+hipError_t launch_widen_int4(const int8_t* P, int64_t ldp, int64_t rows, int64_t K, int8_t* Q,
+                             hipStream_t stream) {
+  const int64_t groups = (K + 31) / 32;
+  const int64_t n = rows * groups;
+  if (n > 0)
+    hipLaunchKernelGGL(widen_int4_kernel, dim3((unsigned int)((n + 255) / 256)), dim3(256), 0, stream, P, ldp,
+                       rows, groups, Q, int4_widened_ld(K));
+  return hipGetLastError();
+}
+
+bool int4_direct_requested() {
+  const char* v = getenv("I8G_INT4_DIRECT");
+  return v && v[0] == '1';
+}
+
 }  // namespace i8g

@@ -61,7 +61,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent);
 GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent, int force_tile,
                           int force_splits);
 // Validates, plans and enqueues one GEMM exactly as gemm_i8_blockscaled does
-// (force_tile / force_splits as in plan_gemm_forced).
+// (force_tile / force_splits as in plan_gemm_forced; force_tile == -2 is the
+// library's own choice, -3 the direct int4 kernel for int4 operands).
 int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt, int64_t ldb,
                  const float* s_col, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
                  uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,
@@ -71,6 +72,14 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
 // I8G_FORCE_SPLITS).
 GemmPlan plan_gemm_int4(int64_t M, int64_t N, int64_t K, int force_splits);
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
+// int4 operands are by default widened to int8 codes in the workspace (rows
+// of int4_widened_ld(K) bytes) and multiplied by the int8 kernels;
+// I8G_INT4_DIRECT=1 (tests) selects gemm_i4_kernel, which reads the packed
+// bytes itself.
+int64_t int4_widened_ld(int64_t K);
+hipError_t launch_widen_int4(const int8_t* P, int64_t ldp, int64_t rows, int64_t K, int8_t* Q,
+                             hipStream_t stream);
+bool int4_direct_requested();
 // Requantizing epilogue: one K split, a non-persistent tile (I8G_FORCE_TILE
 // 0..2 honoured for tests); the workspace adds M words of row maxima.
 GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K);

@@ -84,13 +84,23 @@ def _upload_int8(codes):
 GSHAPES = [(1, 1, 1), (17, 33, 15), (130, 190, 70), (300, 520, 192), (256, 256, 1000), (129, 65, 4097)]
 
 
+@pytest.fixture(params=["widened", "direct"])
+def int4_path(request):
+    """int4 operands widened to int8 for the int8 kernels (the default), or
+    read packed by gemm_i4_kernel (I8G_INT4_DIRECT=1)."""
+    if request.param == "direct":
+        os.environ["I8G_INT4_DIRECT"] = "1"
+    yield request.param
+    os.environ.pop("I8G_INT4_DIRECT", None)
+
+
 @pytest.mark.parametrize("combo", [(True, False), (False, True), (True, True)])
 @pytest.mark.parametrize("shape", GSHAPES)
-def test_gemm_int4_operands(g, combo, shape):
+def test_gemm_int4_operands(g, combo, shape, int4_path):
     a4, b4 = combo
     M, N, K = shape
     relu = (M + N) % 2 == 1
-    say("gemm int4", a4, b4, M, N, K, relu)
+    say("gemm int4", int4_path, a4, b4, M, N, K, relu)
     rng = np.random.default_rng(M * 31 + N * 7 + K)
     A = rng.standard_t(3, (M, K)).astype(np.float32)
     B = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
@@ -107,7 +117,7 @@ def test_gemm_int4_operands(g, combo, shape):
     assert g.hash_value(h) == hashref.output_hash(C_ref)
 
 
-def test_gemm_int4_forced_splits(g):
+def test_gemm_int4_forced_splits(g, int4_path):
     """Split K with int4 operands (the partial sums are shifted back before
     they are stored, so the combine is the int8 one)."""
     M, N, K = 96, 200, 4160
@@ -131,7 +141,7 @@ def test_gemm_int4_forced_splits(g):
         del os.environ["I8G_FORCE_SPLITS"]
 
 
-def test_whole_method_int4_weights_mlp_down(g):
+def test_whole_method_int4_weights_mlp_down(g, int4_path):
     """GPT-2-small MLP down-projection shape (2048 tokens) with int4 / pow2
     weights quantized on the device, activations int8: every step on the
     GPU, compared with the oracle bit for bit."""
