@@ -277,6 +277,42 @@ def test_long_k_split(g):
     check_against_oracle(got, A, B, relu=False)
 
 
+@pytest.mark.parametrize("splits", [0, 7])
+def test_max_k_int32_limit(g, splits):
+    """K = 133144, the largest K whose sums of +-127 * +-127 products stay in
+    int32: codes all +-127 put |acc| within 127^2 of 2^31 - 1 (and above
+    2^24, so RN(acc) rounds), unsplit and over forced K splits whose partial
+    sums are combined exactly."""
+    M, N, K = 48, 40, ref.K_MAX
+    rng = np.random.default_rng(133144)
+    QA = np.where(rng.random((M, K)) < 0.5, 127, -127).astype(np.int8)
+    QB = np.where(rng.random((N, K)) < 0.5, 127, -127).astype(np.int8)
+    QA[0] = 127
+    QB[0] = 127                           # acc[0, 0] = 127^2 K = 2147479576
+    QB[1] = -127                          # acc[0, 1] = -2147479576
+    sr = (rng.random(M) + 0.5).astype(F32)
+    sc = (rng.random(N) * 1e-9 + 1e-10).astype(F32)
+    want = ref.gemm_i8_blockscaled(QA, sr, QB, sc)
+    acc = ref.accumulate(QA, QB)
+    assert acc[0, 0] == 127 * 127 * K and acc[0, 1] == -127 * 127 * K
+    ld = (K + 15) // 16 * 16
+    dA = torch.zeros((M, ld), dtype=torch.int8, device="cuda")
+    dB = torch.zeros((N, ld), dtype=torch.int8, device="cuda")
+    dA[:, :K] = torch.from_numpy(QA).cuda()
+    dB[:, :K] = torch.from_numpy(QB).cuda()
+    say("max K", M, N, K, "splits", splits)
+    if splits:
+        os.environ["I8G_FORCE_SPLITS"] = str(splits)
+    try:
+        C, h = g.gemm_i8_blockscaled(dA[:, :K], torch.from_numpy(sr).cuda(), dB[:, :K],
+                                     torch.from_numpy(sc).cuda(), want_hash=True)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("I8G_FORCE_SPLITS", None)
+    assert np.array_equal(C.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert g.hash_value(h) == hashref.output_hash(want)
+
+
 # ---------------------------------------------------------------------------
 # hash, errors, workspace
 # ---------------------------------------------------------------------------
