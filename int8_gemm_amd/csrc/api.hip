@@ -3,6 +3,7 @@
 // on the caller's stream.  No device memory is allocated here.
 #include <stdint.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/int8_gemm.h"
@@ -194,6 +195,9 @@ int quantize_batch(const i8g_quantize_job* jobs, int32_t n, void* stream) {
     if (e != hipSuccess) return I8G_EHIP;
   }
   if (batch.empty()) return I8G_OK;
+  // workgroups start in id order: the column passes, whose workgroups each
+  // hold a whole band and run longest, go first
+  std::stable_partition(batch.begin(), batch.end(), [](const QJob& q) { return q.kind == QK_COLS_REG; });
   return hip_status(launch_quantize_batch(batch.data(), (int)batch.size(), st));
 }
 

@@ -92,7 +92,10 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
                                 int8_t* Q, int64_t ldq, float* scale, int fmt, hipStream_t stream);
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                 int8_t* Qt, int64_t ldqt, float* scale, int fmt, hipStream_t stream);
-// One quantize pass of quantize_batch (planned by plan_qjob).
+// One quantize pass of quantize_batch (planned by plan_qjob): a row pass
+// with a wave per row, a row pass with a workgroup per row, or a column pass
+// with a workgroup per band of columns.
+enum QKind : int { QK_ROWS_WAVE = 0, QK_ROWS_BLOCK = 1, QK_COLS_REG = 2 };
 struct QJob {
   const float* X;
   int8_t* Q;

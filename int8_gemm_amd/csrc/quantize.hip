@@ -625,7 +625,6 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
 // with its index inside the range.  Small passes, bound by latency alone,
 // then share the chip instead of following one another.
 // ---------------------------------------------------------------------------
-enum QKind : int { QK_ROWS_WAVE = 0, QK_ROWS_BLOCK = 1, QK_COLS_REG = 2 };
 
 template <int FMT>
 __device__ __forceinline__ void run_qjob(const QJob& q, int bid, char* smem) {
