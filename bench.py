@@ -302,12 +302,13 @@ def cpu_baseline(tensors, gemms, ops, budget_s=10.0, fmt_b=0):
 # traffic from committed PMC summaries (null unless the kernels are unchanged)
 # ---------------------------------------------------------------------------
 def kernel_source_sha():
-    """Digest of the sources the timed kernels are built from (the self-check
-    code in verify.hip launches none of them)."""
+    """Digest of the sources the timed kernels and their planner are built
+    from (api.hip holds the host-side argument checks and verify.hip the
+    self-checks; neither changes a kernel)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int8_gemm_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f == "verify.hip":
+        if f in ("verify.hip", "api.hip"):
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
