@@ -44,3 +44,46 @@ def test_host_only_calls(repo_root):
     # argument errors are reported before anything is enqueued
     assert lib.quantize_rows(None, -1, 2, 2, None, 2, None, None) == 1
     assert lib.output_hash(None, 1, 1, 1, None, None, 0, None) == 1
+
+
+def test_argument_checks_of_the_extended_entry_points():
+    """Validation happens on the host before anything is enqueued, so these
+    calls return their status without a device."""
+    import int8_gemm_amd as g
+    lib = g.load()
+    P = ctypes.c_void_p
+    fake = P(1 << 20)                      # never dereferenced: every call below fails validation
+    # quantize_*_fmt: unknown format bit, negative size, ld below the (int4) line length
+    assert lib.quantize_rows_fmt(fake, 4, 40, 40, fake, 40, fake, 4, None) == 1
+    assert lib.quantize_cols_fmt(fake, -1, 4, 4, fake, 4, fake, 0, None) == 1
+    assert lib.quantize_rows_fmt(fake, 4, 40, 40, fake, 16, fake, 2, None) == 1    # needs 32 bytes
+    assert lib.quantize_cols_fmt(fake, 40, 4, 4, fake, 16, fake, 2, None) == 1     # needs 32 bytes
+    assert lib.quantize_rows_fmt(fake, 4, 40, 40, P((1 << 20) + 1), 32, fake, 2, None) == 3
+    assert lib.quantize_rows_fmt(fake, 4, 40, 40, fake, 40, None, 0, None) == 1    # null scale
+    assert lib.quantize_rows_fmt(None, 0, 40, 40, None, 40, None, 0, None) == 0    # nothing to do
+    # quantize_batch: bad count, null array, a bad job stops the whole batch
+    assert lib.quantize_batch(None, -1, None) == 1
+    assert lib.quantize_batch(None, 2, None) == 1
+    assert lib.quantize_batch(None, 0, None) == 0
+    jobs = (g.QuantizeJob * 2)(g.QuantizeJob(fake.value, 4, 40, 40, fake.value, 40, fake.value, 0, 0),
+                               g.QuantizeJob(fake.value, 4, 40, 40, fake.value, 3, fake.value, 1, 0))
+    assert lib.quantize_batch(jobs, 2, None) == 1          # job 1: its lines (columns) hold 4 values, ldq 3
+    # gemm: unknown flag, K beyond the int32 range, int4 operand ld below 16*ceil(K/32)
+    ws = P(1 << 24)
+    assert lib.gemm_i8_blockscaled(fake, 16, fake, fake, 16, fake, 4, 4, 4, fake, 4, 16, None, ws, 1 << 20, None) == 1
+    assert lib.gemm_i8_blockscaled(fake, 16, fake, fake, 16, fake, 4, 4, 133145, fake, 4, 0, None, ws, 1 << 20, None) == 2
+    assert lib.gemm_i8_blockscaled(fake, 16, fake, fake, 16, fake, 4, 4, 64, fake, 4, 4, None, ws, 1 << 20, None) == 3
+    # requant: unknown flag, null outputs, ldq < N, misaligned workspace
+    assert lib.gemm_i8_requant(fake, 16, fake, fake, 16, fake, 4, 4, 4, fake, 4, fake, 4, None, ws, 1 << 20, None) == 1
+    assert lib.gemm_i8_requant(fake, 16, fake, fake, 16, fake, 4, 4, 4, None, 4, fake, 0, None, ws, 1 << 20, None) == 1
+    assert lib.gemm_i8_requant(fake, 16, fake, fake, 16, fake, 4, 5, 4, fake, 4, fake, 0, None, ws, 1 << 20, None) == 1
+    assert lib.gemm_i8_requant(fake, 16, fake, fake, 16, fake, 4, 4, 4, fake, 4, fake, 0, None, P(1 << 20 | 8), 1 << 20, None) == 4
+    # workspace sizes: int4 operands need room for their widened copies
+    M, N, K = 512, 768, 3072
+    base = lib.gemm_i8_workspace_bytes(M, N, K)
+    assert lib.gemm_i8_workspace_bytes_flags(M, N, K, 0) == base
+    assert lib.gemm_i8_workspace_bytes_flags(M, N, K, 8) >= N * K
+    assert lib.gemm_i8_workspace_bytes_flags(M, N, K, 12) >= (M + N) * K
+    assert lib.gemm_i8_requant_workspace_bytes(M, N, K) >= 256 + 4 * M
+    assert lib.gemm_i8_requant_workspace_bytes(0, N, K) == 256
+    assert lib.i8g_status_string(6).startswith(b"self-check failed")
