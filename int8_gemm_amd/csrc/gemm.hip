@@ -1252,7 +1252,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // ---- direct-to-LDS loads: lane l of a load fills row l/8, position l%8 ----
   const int r_in = lane >> 3, pch = lane & 7;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int wm_s = wave_s / WAVES_N, wn_s = wave_s % WAVES_N;
+  const int wm_s = wave_s / WAVES_N;
   // Loads go through buffer resources: the tile (and stage) base is scalar,
   // and each lane's offset is the same for every tile.  B rows at or beyond N
   // and column scales at or beyond N fall outside the resource's range and
@@ -1444,21 +1444,6 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   };
   // Element 4q+e of block b = (i, j) of accumulator set Y: lane l holds
   // column l % 32 and row 8q + 4*(l/32) + e of the block.
-  auto drain_elem = [&](v16i (&Y)[FM][FN], const Out& o, const DHalf& d, int scb, auto IJ, auto Q, auto E)
-      __attribute__((always_inline)) {
-    constexpr int b = decltype(IJ)::value, q = decltype(Q)::value, e = decltype(E)::value;
-    constexpr int i = b / FN, j = b % FN;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(o.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
-        0x00020000);
-    float y = epilogue1(Y[i][j][q * 4 + e], __int_as_float(d.sr[q % 2][e]), __int_as_float(scb));
-    if (RELU) y = relu_pos0(y);
-    tcol[j] += (uint64_t)(unsigned int)d.rk[q % 2][e] * (uint64_t)__float_as_uint(y);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, o.voff[j], (q * 8 + e) * (int)ldc4, 0);
-    // keep the hash terms where they are computed: summed later, they would
-    // keep every y alive
-    if constexpr (e == 3) asm volatile("" : "+v"(tcol[j]));
-  };
   // The four elements of part q of block b = (i, j), in steps spread over the
   // slots of a k-step so that the four dependency chains overlap each other
   // and the MFMAs: step 0 converts the accumulators, 1 applies the row

@@ -573,7 +573,7 @@ int gate_gemm_int4(GateRun& g, const G4Case& c, int case_id, int* ncases) {
 // The requantizing epilogue: codes and scales must be the mirror's per-row
 // quantization of the mirror's output, and the hash that output's hash.
 int gate_requant(GateRun& g, int* ncases) {
-  const int64_t M = 300, N = 520, K = 192, ld = round16(K);
+  const int64_t M = 300, N = 520, K = 192;
   std::vector<float> A(M * K), B(N * K);
   for (int64_t e = 0; e < M * K; ++e) A[e] = mirror::gate_value(0x6E5A0000ull, e);
   for (int64_t e = 0; e < N * K; ++e) B[e] = mirror::gate_value(0x6E5B0000ull, e);
@@ -605,7 +605,6 @@ int gate_requant(GateRun& g, int* ncases) {
   const size_t wsb = gemm_i8_requant_workspace_bytes(M, N, K);
   char* gw = g.take(wsb);
   if (g.cursor > kGateWorkspace) return I8G_EWORKSPACE;
-  (void)ld;
   if (!st) st = hipok(hipMemcpyAsync(dsr, sr.data(), M * 4, hipMemcpyHostToDevice, g.st));
   if (!st) st = hipok(hipMemcpyAsync(dsc, sc.data(), N * 4, hipMemcpyHostToDevice, g.st));
   if (st) return st;
