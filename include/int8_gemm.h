@@ -325,7 +325,8 @@ int i8g_gate(void* workspace, size_t workspace_bytes, void* stream, i8g_gate_rep
  * i8g_audit_gemm -- live audit of one GEMM output: `samples` cells (i, j),
  * drawn from SplitMix64(seed), are recomputed on the device with a scalar
  * dot product (not the MFMA path) and the epilogue, and compared bit for bit
- * with C.  Arguments as gemm_i8_blockscaled (I8G_HASH in flags is ignored).
+ * with C.  Arguments as gemm_i8_blockscaled (I8G_HASH in flags is ignored;
+ * I8G_A_INT4 / I8G_B_INT4 read int4 operands in their packed layout).
  *   result  device pointer to two uint64_t: result[0] = number of sampled
  *           cells that differ, result[1] = smallest i*N + j among them
  *           (UINT64_MAX if none).  Written by the call's own kernels.
@@ -347,6 +348,13 @@ int i8g_audit_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8
 int i8g_audit_quantize(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Q,
                        int64_t ldq, const float* scale, int32_t by_col, uint64_t seed,
                        int32_t samples, uint64_t* result, void* stream);
+/* The same for an output of quantize_rows_fmt / quantize_cols_fmt in
+ * `format` (int4 lines: every value and the zero nibbles after the last one
+ * in its 16-byte group are checked). */
+int i8g_audit_quantize_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                           const int8_t* Q, int64_t ldq, const float* scale, int32_t by_col,
+                           uint32_t format, uint64_t seed, int32_t samples, uint64_t* result,
+                           void* stream);
 
 /* Bytes of workspace i8g_probe_hash needs for this shape. */
 size_t i8g_probe_workspace_bytes(int64_t M, int64_t N, int64_t K);

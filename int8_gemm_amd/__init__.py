@@ -42,7 +42,7 @@ EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_wo
             "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
             "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt",
             "gemm_i8_requant", "gemm_i8_requant_workspace_bytes", "quantize_batch",
-            "gemm_i8_workspace_bytes_flags")
+            "gemm_i8_workspace_bytes_flags", "i8g_audit_quantize_fmt")
 
 _lib = None
 _ws = {}
@@ -108,6 +108,9 @@ def load():
     lib.i8g_audit_quantize.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, ctypes.c_int32,
                                        ctypes.c_uint64, ctypes.c_int32, c_vp, c_vp]
     lib.i8g_audit_quantize.restype = ctypes.c_int
+    lib.i8g_audit_quantize_fmt.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, ctypes.c_int32, c_u32,
+                                           ctypes.c_uint64, ctypes.c_int32, c_vp, c_vp]
+    lib.i8g_audit_quantize_fmt.restype = ctypes.c_int
     lib.i8g_probe_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
     lib.i8g_probe_workspace_bytes.restype = c_sz
     lib.i8g_probe_hash.argtypes = [ctypes.c_uint64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
@@ -355,27 +358,35 @@ def gate(device=None):
     return rc, rep.as_dict()
 
 
-def audit_gemm(QA, s_row, QBt, s_col, C, relu=False, seed=0, samples=1024):
+def audit_gemm(QA, s_row, QBt, s_col, C, relu=False, seed=0, samples=1024, K=None, a_int4=False,
+               b_int4=False):
     """i8g_audit_gemm on a GEMM output: returns a 2-element int64 device
-    tensor (number of differing sampled cells, smallest i*N + j of them or -1)."""
-    M, K = QA.shape
+    tensor (number of differing sampled cells, smallest i*N + j of them or -1).
+    With int4 operands (packed lines) K must be given."""
+    M, ka = QA.shape
     N = QBt.shape[0]
+    if K is None:
+        if a_int4 or b_int4:
+            raise ValueError("K is required with int4 operands")
+        K = ka
+    flags = (I8G_RELU if relu else 0) | (I8G_A_INT4 if a_int4 else 0) | (I8G_B_INT4 if b_int4 else 0)
     r = torch.empty(2, dtype=torch.int64, device=C.device)
     _check(load().i8g_audit_gemm(
         _ptr(QA), QA.stride(0) if M > 0 else _round16(K), _ptr(s_row), _ptr(QBt),
         QBt.stride(0) if N > 0 else _round16(K), _ptr(s_col), M, N, K, _ptr(C), max(C.stride(0), N, 1),
-        I8G_RELU if relu else 0, seed & ((1 << 64) - 1), samples, _ptr(r), _stream(C)))
+        flags, seed & ((1 << 64) - 1), samples, _ptr(r), _stream(C)))
     return r
 
 
-def audit_quantize(X, Q, scale, by_col, seed=0, samples=64):
-    """i8g_audit_quantize: X with its quantize_rows (by_col=False) or
-    quantize_cols (by_col=True) output; returns as audit_gemm (lines)."""
+def audit_quantize(X, Q, scale, by_col, seed=0, samples=64, fmt=0):
+    """i8g_audit_quantize_fmt: X with its quantize_rows_fmt (by_col=False) or
+    quantize_cols_fmt (by_col=True) output in format ``fmt``; returns as
+    audit_gemm (lines)."""
     rows, cols = X.shape
     r = torch.empty(2, dtype=torch.int64, device=X.device)
-    _check(load().i8g_audit_quantize(
+    _check(load().i8g_audit_quantize_fmt(
         _ptr(X), rows, cols, max(X.stride(0), cols, 1), _ptr(Q), max(Q.stride(0), 1), _ptr(scale),
-        1 if by_col else 0, seed & ((1 << 64) - 1), samples, _ptr(r), _stream(X)))
+        1 if by_col else 0, fmt, seed & ((1 << 64) - 1), samples, _ptr(r), _stream(X)))
     return r
 
 

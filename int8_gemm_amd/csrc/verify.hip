@@ -185,11 +185,21 @@ __global__ void audit_init_kernel(unsigned long long* r) {
   }
 }
 
+// Value k of a stored line: int8, or int4 in the layout of
+// quantize_rows_fmt (byte 16*(k/32) + k%16, low nibble for k%32 < 16, else
+// high; 4-bit two's complement).
+__device__ __forceinline__ int code_at(const int8_t* line, int64_t k, int int4) {
+  if (!int4) return line[k];
+  const int b = (unsigned char)line[16 * (k / 32) + k % 16];
+  const int n = (k % 32) < 16 ? (b & 0xF) : (b >> 4);
+  return n >= 8 ? n - 16 : n;
+}
+
 __global__ void __launch_bounds__(256)
 audit_gemm_kernel(const int8_t* __restrict__ QA, int64_t lda, const float* __restrict__ s_row,
                   const int8_t* __restrict__ QB, int64_t ldb, const float* __restrict__ s_col,
                   int64_t M, int64_t N, int64_t K, const float* __restrict__ C, int64_t ldc, int relu,
-                  uint64_t seed, int samples, unsigned long long* r) {
+                  int a4, int b4, uint64_t seed, int samples, unsigned long long* r) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= samples) return;
   const uint64_t h = splitmix64_at(seed, (uint64_t)s);
@@ -199,6 +209,9 @@ audit_gemm_kernel(const int8_t* __restrict__ QA, int64_t lda, const float* __res
   const int8_t* b = QB + j * ldb;
   int32_t acc = 0;
   int64_t k = 0;
+  if (a4 || b4) {
+    for (; k < K; ++k) acc += code_at(a, k, a4) * code_at(b, k, b4);
+  }
   for (; k + 4 <= K; k += 4) {   // rows are 16-byte aligned (lda, ldb multiples of 16)
     const int av = *reinterpret_cast<const int*>(a + k);
     const int bv = *reinterpret_cast<const int*>(b + k);
@@ -219,7 +232,7 @@ audit_gemm_kernel(const int8_t* __restrict__ QA, int64_t lda, const float* __res
 __global__ void __launch_bounds__(256)
 audit_quantize_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
                       const int8_t* __restrict__ Q, int64_t ldq, const float* __restrict__ scale,
-                      int by_col, uint64_t seed, unsigned long long* r) {
+                      int by_col, int fmt, uint64_t seed, unsigned long long* r) {
   __shared__ float red[4];
   __shared__ int bad_any;
   const int64_t nlines = by_col ? cols : rows, len = by_col ? rows : cols;
@@ -232,11 +245,20 @@ audit_quantize_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, i
   if (threadIdx.x == 0) bad_any = 0;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = scale_of_absmax(a);
+  const float s = fmt == 0 ? scale_of_absmax_fmt<0>(a)
+                  : fmt == FMT_POW2 ? scale_of_absmax_fmt<FMT_POW2>(a)
+                  : fmt == FMT_INT4 ? scale_of_absmax_fmt<FMT_INT4>(a)
+                                    : scale_of_absmax_fmt<FMT_INT4 | FMT_POW2>(a);
   const float inv = recip_rn(s);
+  const int int4 = (fmt & FMT_INT4) != 0;
   int bad = (threadIdx.x == 0) && (__float_as_uint(s) != __float_as_uint(scale[line]));
-  for (int64_t e = threadIdx.x; e < len; e += 256)
-    if (quantize1(xat(e), inv) != (int)Q[line * ldq + e]) bad = 1;
+  // int4 lines: the nibbles after the last value (to the end of its 16-byte
+  // group) must be 0 as well
+  const int64_t stored = int4 ? (len + 31) / 32 * 32 : len;
+  for (int64_t e = threadIdx.x; e < stored; e += 256) {
+    const int want = e < len ? quantize1(xat(e), inv) : 0;
+    if (code_at(Q + line * ldq, e, int4) != want) bad = 1;
+  }
   if (bad) atomicOr(&bad_any, 1);
   __syncthreads();
   if (threadIdx.x == 0 && bad_any) {
@@ -677,33 +699,43 @@ int i8g_audit_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8
                    const float* s_col, int64_t M, int64_t N, int64_t K, const float* C, int64_t ldc,
                    uint32_t flags, uint64_t seed, int32_t samples, uint64_t* result, void* stream) {
   if (M < 0 || N < 0 || K < 0 || samples < 0 || !result) return I8G_EINVAL;
-  if (flags & ~(uint32_t)(I8G_RELU | I8G_HASH)) return I8G_EINVAL;
+  if (flags & ~(uint32_t)(I8G_RELU | I8G_HASH | I8G_A_INT4 | I8G_B_INT4)) return I8G_EINVAL;
+  const int a4 = (flags & I8G_A_INT4) ? 1 : 0, b4 = (flags & I8G_B_INT4) ? 1 : 0;
+  const int64_t k4 = (K + 31) / 32 * 16;
   const hipStream_t st = as_stream(stream);
   unsigned long long* r = reinterpret_cast<unsigned long long*>(result);
   hipLaunchKernelGGL(audit_init_kernel, dim3(1), dim3(64), 0, st, r);
   if (M == 0 || N == 0 || samples == 0) return hipGetLastError() == hipSuccess ? I8G_OK : I8G_EHIP;
   if (!s_row || !s_col || !C || ldc < N || (K > 0 && (!QA || !QBt))) return I8G_EINVAL;
-  if (K > 0 && (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < K ||
-                ldb < K))
+  if (K > 0 && (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) ||
+                lda < (a4 ? k4 : K) || ldb < (b4 ? k4 : K)))
     return I8G_EALIGN;
   hipLaunchKernelGGL(audit_gemm_kernel, dim3((samples + 255) / 256), dim3(256), 0, st, QA, lda, s_row, QBt,
-                     ldb, s_col, M, N, K, C, ldc, (flags & I8G_RELU) ? 1 : 0, seed, samples, r);
+                     ldb, s_col, M, N, K, C, ldc, (flags & I8G_RELU) ? 1 : 0, a4, b4, seed, samples, r);
+  return hipGetLastError() == hipSuccess ? I8G_OK : I8G_EHIP;
+}
+
+int i8g_audit_quantize_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Q,
+                           int64_t ldq, const float* scale, int32_t by_col, uint32_t format, uint64_t seed,
+                           int32_t samples, uint64_t* result, void* stream) {
+  if (rows < 0 || cols < 0 || samples < 0 || !result) return I8G_EINVAL;
+  if (format & ~(uint32_t)(I8G_FMT_POW2 | I8G_FMT_INT4)) return I8G_EINVAL;
+  const hipStream_t st = as_stream(stream);
+  unsigned long long* r = reinterpret_cast<unsigned long long*>(result);
+  hipLaunchKernelGGL(audit_init_kernel, dim3(1), dim3(64), 0, st, r);
+  const int64_t nlines = by_col ? cols : rows, len = by_col ? rows : cols;
+  if (nlines == 0 || samples == 0) return hipGetLastError() == hipSuccess ? I8G_OK : I8G_EHIP;
+  const int64_t line_bytes = (format & I8G_FMT_INT4) ? (len + 31) / 32 * 16 : len;
+  if (!scale || (len > 0 && (!X || !Q)) || ldx < cols || ldq < line_bytes) return I8G_EINVAL;
+  hipLaunchKernelGGL(audit_quantize_kernel, dim3(samples), dim3(256), 0, st, X, rows, cols, ldx, Q, ldq,
+                     scale, by_col ? 1 : 0, (int)format, seed, r);
   return hipGetLastError() == hipSuccess ? I8G_OK : I8G_EHIP;
 }
 
 int i8g_audit_quantize(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Q,
                        int64_t ldq, const float* scale, int32_t by_col, uint64_t seed, int32_t samples,
                        uint64_t* result, void* stream) {
-  if (rows < 0 || cols < 0 || samples < 0 || !result) return I8G_EINVAL;
-  const hipStream_t st = as_stream(stream);
-  unsigned long long* r = reinterpret_cast<unsigned long long*>(result);
-  hipLaunchKernelGGL(audit_init_kernel, dim3(1), dim3(64), 0, st, r);
-  const int64_t nlines = by_col ? cols : rows, len = by_col ? rows : cols;
-  if (nlines == 0 || samples == 0) return hipGetLastError() == hipSuccess ? I8G_OK : I8G_EHIP;
-  if (!scale || (len > 0 && (!X || !Q)) || ldx < cols || ldq < len) return I8G_EINVAL;
-  hipLaunchKernelGGL(audit_quantize_kernel, dim3(samples), dim3(256), 0, st, X, rows, cols, ldx, Q, ldq,
-                     scale, by_col ? 1 : 0, seed, r);
-  return hipGetLastError() == hipSuccess ? I8G_OK : I8G_EHIP;
+  return i8g_audit_quantize_fmt(X, rows, cols, ldx, Q, ldq, scale, by_col, 0u, seed, samples, result, stream);
 }
 
 size_t i8g_probe_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -88,3 +88,43 @@ def test_probe_hash_matches_oracle(g, case):
     say("probe", seed, M, N, K)
     h = g.hash_value(g.probe_hash(seed, M, N, K))
     assert h == probe.probe_hash(seed, M, N, K)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_audit_quantize_formats(g, fmt):
+    """The live quantize audit on pow2 / int4 outputs: clean, then with one
+    packed byte (int4) or code changed in line 9."""
+    rng = np.random.default_rng(30 + fmt)
+    X = torch.from_numpy(rng.standard_t(3, (200, 333)).astype(np.float32)).cuda()
+    for by_col in (False, True):
+        say("audit quantize fmt", fmt, "by_col", by_col)
+        Q, s = (g.quantize_cols_fmt if by_col else g.quantize_rows_fmt)(X, fmt)
+        lines = s.numel()
+        r = g.audit_quantize(X, Q, s, by_col, seed=5, samples=16 * lines, fmt=fmt)
+        torch.cuda.synchronize()
+        assert r[0].item() == 0 and r[1].item() == -1
+        bad = Q.clone()
+        bad[9, 3] = bad[9, 3] ^ 0x11          # one code (int4: two nibbles) changed
+        r = g.audit_quantize(X, bad, s, by_col, seed=5, samples=16 * lines, fmt=fmt)
+        torch.cuda.synchronize()
+        assert r[0].item() > 0 and r[1].item() == 9
+
+
+@pytest.mark.parametrize("combo", [(False, True), (True, True)])
+def test_audit_gemm_int4_operands(g, combo):
+    a4, b4 = combo
+    M, N, K = 130, 190, 333
+    rng = np.random.default_rng(44)
+    A = torch.from_numpy(rng.standard_t(3, (M, K)).astype(np.float32)).cuda()
+    B = torch.from_numpy((rng.standard_normal((K, N)) * 0.02).astype(np.float32)).cuda()
+    QA, sr = g.quantize_rows_fmt(A, 2 if a4 else 0)
+    QB, sc = g.quantize_cols_fmt(B, 2 if b4 else 0)
+    C = g.gemm_i8_blockscaled(QA, sr, QB, sc, relu=True, K=K, a_int4=a4, b_int4=b4)
+    say("audit gemm int4", a4, b4)
+    r = g.audit_gemm(QA, sr, QB, sc, C, relu=True, seed=2, samples=20000, K=K, a_int4=a4, b_int4=b4)
+    torch.cuda.synchronize()
+    assert r[0].item() == 0
+    C2 = torch.nextafter(C, torch.full_like(C, float("inf")))
+    r = g.audit_gemm(QA, sr, QB, sc, C2, relu=True, seed=2, samples=1000, K=K, a_int4=a4, b_int4=b4)
+    torch.cuda.synchronize()
+    assert r[0].item() == 1000
