@@ -416,18 +416,45 @@ __device__ __forceinline__ void qcols_reg_body(const float* __restrict__ X, int6
     }
   }
   __syncthreads();
-  // store: BC rows of Qt, rows bytes each, 16 bytes per thread
-  const int r16 = rp / 16;
-  for (int q = tid; q < BC * r16; q += QCR_THREADS) {
-    const int c = q / r16, off = (q % r16) * 16;
-    const int64_t j = j0 + c;
-    if (j >= cols) continue;
-    int8_t* dst = Qt + j * ldqt + off;
-    const int8_t* src = tile + c * rp + off;
-    if (vec_out && off + 16 <= rows) {
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-    } else {
-      for (int e = 0; e < 16 && off + e < rows; ++e) dst[e] = src[e];
+  if constexpr ((FMT & FMT_INT4) != 0) {
+    // int4 lines: a thread per 16-byte group of 32 values (low nibbles values
+    // 0-15, high nibbles 16-31; zero past the line's end); Qt is 16-byte
+    // aligned with ldqt a multiple of 16 for this format
+    const int g4 = (int)((rows + 31) / 32);
+    for (int q = tid; q < BC * g4; q += QCR_THREADS) {
+      const int c = q / g4, gi = q % g4;
+      const int64_t j = j0 + c;
+      if (j >= cols) continue;
+      const int8_t* src = tile + c * rp;
+      unsigned int w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        unsigned int v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int k0 = gi * 32 + 4 * i + b, k1 = k0 + 16;
+          const unsigned int lo = k0 < rows ? ((unsigned int)src[k0] & 0xFu) : 0u;
+          const unsigned int hi = k1 < rows ? ((unsigned int)src[k1] & 0xFu) : 0u;
+          v |= (lo | (hi << 4)) << (8 * b);
+        }
+        w[i] = v;
+      }
+      *reinterpret_cast<uint4*>(Qt + j * ldqt + gi * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    // store: BC rows of Qt, rows bytes each, 16 bytes per thread
+    const int r16 = rp / 16;
+    for (int q = tid; q < BC * r16; q += QCR_THREADS) {
+      const int c = q / r16, off = (q % r16) * 16;
+      const int64_t j = j0 + c;
+      if (j >= cols) continue;
+      int8_t* dst = Qt + j * ldqt + off;
+      const int8_t* src = tile + c * rp + off;
+      if (vec_out && off + 16 <= rows) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int e = 0; e < 16 && off + e < rows; ++e) dst[e] = src[e];
+      }
     }
   }
 }
@@ -581,6 +608,21 @@ template <int FMT>
 hipError_t quantize_cols_int4(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
                               int64_t ldqt, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
+  // up to 8192 rows: the one-kernel band path, packing as it stores
+  int bc = rows > 0 ? qcols_band(rows, cols) : 0;
+  const char* force = getenv("I8G_QCOLS_TWO_PASS");
+  if (force && force[0] == '1') bc = 0;
+  if (bc > 0) {
+    const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
+    switch (bc) {
+      case 64: hipLaunchKernelGGL((qcols_reg_kernel<64, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, 1); break;
+      case 32: hipLaunchKernelGGL((qcols_reg_kernel<32, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, 1); break;
+      case 16: hipLaunchKernelGGL((qcols_reg_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, 1); break;
+      case 8: hipLaunchKernelGGL((qcols_reg_kernel<8, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, 1); break;
+      default: hipLaunchKernelGGL((qcols_reg_kernel<4, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Qt, ldqt, scale, vec_in, 1); break;
+    }
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(qcols_init_kernel<FMT>, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
                      stream, scale, cols);
   if (rows > 0) {
@@ -628,6 +670,16 @@ hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int6
 
 template <int FMT>
 __device__ __forceinline__ void run_qjob(const QJob& q, int bid, char* smem) {
+  if constexpr ((FMT & FMT_INT4) != 0) {   // int4 jobs are column passes only
+    switch (q.param) {
+      case 64: qcols_reg_body<64, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      case 32: qcols_reg_body<32, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      case 16: qcols_reg_body<16, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      case 8: qcols_reg_body<8, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+      default: qcols_reg_body<4, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid, q.blocks, smem); break;
+    }
+    return;
+  }
   if (q.kind == QK_ROWS_WAVE) {
     switch (q.param) {
       case 1: qrows_wave_body<1, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
@@ -654,15 +706,18 @@ __global__ void __launch_bounds__(1024) quantize_batch_kernel(const QBatch b) {
   const QJob& q = b.job[j];
   const int bid = id - q.first;
   if (bid >= q.blocks) return;   // the padding of the job's range
-  if (q.fmt & FMT_POW2)
-    run_qjob<FMT_POW2>(q, bid, smem);
-  else
-    run_qjob<0>(q, bid, smem);
+  switch (q.fmt) {
+    case 0: run_qjob<0>(q, bid, smem); break;
+    case FMT_POW2: run_qjob<FMT_POW2>(q, bid, smem); break;
+    case FMT_INT4: run_qjob<FMT_INT4>(q, bid, smem); break;
+    default: run_qjob<FMT_INT4 | FMT_POW2>(q, bid, smem); break;
+  }
 }
 
 bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
                float* scale, bool by_col, int fmt, QJob& q) {
-  if ((fmt & FMT_INT4) || rows <= 0 || cols <= 0) return false;
+  if (rows <= 0 || cols <= 0) return false;
+  if ((fmt & FMT_INT4) && !by_col) return false;   // int4 rows: their own kernel
   q.X = X; q.Q = Q; q.scale = scale;
   q.rows = rows; q.cols = cols; q.ldx = ldx; q.ldq = ldq;
   q.fmt = fmt;

@@ -172,3 +172,25 @@ def test_format_argument_errors(g):
     assert lib.quantize_rows_fmt(X.data_ptr(), 4, 40, 40, Q.data_ptr(), 16, s.data_ptr(), 2, None) == 1
     # misaligned int4 output
     assert lib.quantize_rows_fmt(X.data_ptr(), 2, 40, 40, Q.data_ptr() + 1, 32, s.data_ptr(), 2, None) == 3
+
+
+@pytest.mark.parametrize("fmt", [F.INT4, F.INT4 | F.POW2])
+@pytest.mark.parametrize("two_pass", [False, True])
+@pytest.mark.parametrize("shape", [(300, 1000), (8192, 40), (9000, 40), (31, 5)])
+def test_int4_columns_both_paths(g, fmt, two_pass, shape):
+    """int4 column passes on the one-kernel band path (up to 8192 rows,
+    packed as they are stored) and on the multi-kernel path (forced here;
+    taken by itself above 8192 rows)."""
+    rows, cols = shape
+    say("int4 cols", fmt, "two_pass", two_pass, rows, cols)
+    X = _data(rows + cols + fmt, rows, cols)
+    if two_pass:
+        os.environ["I8G_QCOLS_TWO_PASS"] = "1"
+    try:
+        Qt, st = g.quantize_cols_fmt(torch.from_numpy(X).cuda(), fmt)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("I8G_QCOLS_TWO_PASS", None)
+    qc, sc = F.quantize_cols(X, fmt)
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), sc.view(np.uint32))
+    assert np.array_equal(_bytes(Qt), F.pack_int4(qc))
