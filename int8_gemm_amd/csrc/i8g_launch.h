@@ -110,7 +110,7 @@ struct QBatch {
   QJob job[kQBatchMax];
   int n;
 };
-// Fills q for an int8 pass the batch kernel can run (false: int4 formats,
+// Fills q for a pass the batch kernel can run (false: int4 row passes,
 // empty shapes, and tall column passes that need several kernels).
 bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Q, int64_t ldq,
                float* scale, bool by_col, int fmt, QJob& q);
