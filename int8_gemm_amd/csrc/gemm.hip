@@ -1153,15 +1153,18 @@ gemm_i8_persist_kernel(const GemmParams p) {
 //  * Direct-to-LDS loads cost per request.  Eight lanes fetching one whole
 //    128-byte line per row feed a CU about twice as fast as four lanes
 //    fetching half a line (about 56 against 29 bytes per clock per CU, all
-//    CUs loading).  A stage therefore holds 128 bytes of K per row, and the
-//    ring has three stages (120 KiB for a 128x192 tile).
-//  * With one wave per SIMD, every wait a wave takes leaves its matrix core
-//    idle.  A stage is four k-steps of six MFMAs per wave.  The fragment reads
-//    of k-step t+1 are issued during k-step t.  Four elements per k-step of the
-//    previous tile's epilogue block (one 32x32 block per stage), and the loads
-//    of stage g+2, are interleaved with the MFMAs.  The stage's only barrier
-//    sits between k-steps 1 and 2, and the scales and row keys that the next
-//    stage's epilogue block needs are read just before it.
+//    CUs loading).  A stage therefore holds 128 bytes of K per row.
+//  * A wave's waits (barrier, loads landing) leave its matrix core idle unless
+//    another wave on the SIMD has MFMAs to issue.  A stage is four k-steps of
+//    FM x FN MFMAs per wave; the fragment reads of k-step t+1 are issued during
+//    k-step t, and four elements per k-step of the previous tile's epilogue
+//    block (one 32x32 block per stage) are interleaved with the MFMAs.  The
+//    stage's only barrier sits before k-step 3: after it the stage's slot is
+//    free, and k-step 3 issues the loads of stage g+STAGES into it.
+// Two configurations: a 128x192 tile, one workgroup per CU and a three-slot
+// ring (120 KiB; the loads have two stages to land), and a 128x128 tile, two
+// workgroups per CU (WPC) and a two-slot ring (64 KiB each; one stage to land,
+// the other workgroup's MFMAs covering the waits).
 // LDS rows are 128 bytes.  Chunk c of row r is stored at position
 // c ^ ((r / 2) % 8), which puts the 16 lanes of each fragment read on
 // distinct banks.
@@ -1197,12 +1200,12 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU, int STAGES, int WPC>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WPC)
 gemm_i8_persist128_kernel(const GemmParams p) {
   constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
   static_assert(NWAVES == 4, "four waves, one per SIMD");
-  constexpr int STAGES = 3;
+  static_assert(STAGES >= 2, "a stage's slot is refilled after the barrier of the stage");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   // wave tiles of whole 32x32 blocks: every fragment row base is then a
   // multiple of 32, which leaves the swizzle phase (row/2)%8 to the lane
@@ -1495,6 +1498,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // slot.  Fixing the order keeps the two fragment sets in distinct registers
   // and the reads one to five MFMAs ahead of their use.
   constexpr int NSLOT = FM * FN;
+  static_assert(NSLOT >= 4, "the epilogue's five steps need at least four slots");
   constexpr int LPSL = (LPS + NSLOT - 2) / (NSLOT - 1);   // loads per slot, slots 0 .. NSLOT-2
   auto kstep = [&](v16i (&X)[FM][FN], const v4i (&fa)[FM], const v4i (&fb)[FN], auto ZERO, int nbuf,
                    int nt, v4i (&na)[FM], v4i (&nb)[FN], auto DMA, const Dma& dm, auto&& slot)
@@ -1559,12 +1563,15 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     auto part = [&](auto Q) __attribute__((always_inline)) {
       return [&, Q](auto MI) __attribute__((always_inline)) {
         constexpr int m = decltype(MI)::value, q = decltype(Q)::value;
-        if constexpr (D && m <= 4) {
+        auto step = [&](auto STEP) __attribute__((always_inline)) {
           if constexpr (q < 2)
-            drain_step(Y, oy, early, scb, BLK, Q, std::integral_constant<int, m>());
+            drain_step(Y, oy, early, scb, BLK, Q, STEP);
           else
-            drain_step(Y, oy, late, scb, BLK, Q, std::integral_constant<int, m>());
-        }
+            drain_step(Y, oy, late, scb, BLK, Q, STEP);
+        };
+        if constexpr (D && m <= 4) step(std::integral_constant<int, m>());
+        // four slots (2x2 blocks per wave): the last one takes steps 3 and 4
+        if constexpr (D && NSLOT == 4 && m == 3) step(std::integral_constant<int, 4>());
       };
     };
     const Dma none{};
@@ -1599,6 +1606,11 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   out_cur.sr_base = out_cur.rk_base = out_cur.sc_base = 0;
   out_cur.col0 = 0;
   out_cur.slot = 0;
+  // Stores of the previous stage issued after the loads a stage waits for:
+  // all sixteen with three or more slots (those loads were issued a stage
+  // earlier), with two slots only the four of its k-step 3 (the loads share
+  // that k-step and precede its stores).
+  constexpr int PREV_ST = STAGES >= 3 ? 16 : 4;
   auto run_tile = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int r, auto DRAIN)
       __attribute__((always_inline)) {
     constexpr bool D = decltype(DRAIN)::value;
@@ -1606,7 +1618,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     const bool has_next = r + 1 < my_tiles;
     static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
       constexpr int b = decltype(BI)::value;
-      constexpr int ST = LPS + (D && b >= 1 ? 16 : 0) + (D ? 12 : 0);
+      constexpr int ST = (STAGES - 2) * LPS + (D && b >= 1 ? PREV_ST : 0) + (D ? 12 : 0);
       DHalf& ec = (b % 2 == 0) ? e0 : e1;
       DHalf& en = (b % 2 == 0) ? e1 : e0;
       int& sc_c = (b % 2 == 0) ? s0 : s1;
@@ -1636,10 +1648,10 @@ gemm_i8_persist128_kernel(const GemmParams p) {
       };
       if (s == NB)
         stage(X, Y, g0 + s, out_prev, e0, s0, late, std::false_type(), std::false_type(),
-              std::integral_constant<int, 0>(), std::integral_constant<int, LPS + (D ? 16 : 0)>(), mid);
+              std::integral_constant<int, 0>(), std::integral_constant<int, (STAGES - 2) * LPS + (D ? PREV_ST : 0)>(), mid);
       else
         stage(X, Y, g0 + s, out_prev, e0, s0, late, std::false_type(), std::false_type(),
-              std::integral_constant<int, 0>(), std::integral_constant<int, LPS>(), mid);
+              std::integral_constant<int, 0>(), std::integral_constant<int, (STAGES - 2) * LPS>(), mid);
     }
   };
 
@@ -1650,11 +1662,11 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     make_out(0, tm, tn, out_cur);
     // prologue: scales and the first three stages of tile 0
     issue_scales(fsrc);
-    issue_ops(0, fsrc, 0);
-    issue_ops(1, fsrc, 1);
-    issue_ops(2, fsrc, 2);
-    fkt = 3;   // nst >= NB >= 3
-    wait_vmcnt_lgkm0<2 * LPS>();   // stage 0 landed; the row keys of tile 0 written
+    static_for<0, STAGES>([&](auto SI) __attribute__((always_inline)) {
+      issue_ops(decltype(SI)::value, fsrc, decltype(SI)::value);
+    });
+    fkt = STAGES;   // nst >= STAGES
+    wait_vmcnt_lgkm0<(STAGES - 1) * LPS>();   // stage 0 landed; the row keys of tile 0 written
     barrier_nofence();
     load_frags(0, 0, fa0, fb0);
 #pragma unroll
@@ -1844,7 +1856,9 @@ splitk_combine_kernel(const GemmParams p) {
 // tiles per workgroup x (MAC time + `tile_overhead`).  The rates were fitted
 // to timings on MI355X of the GPT-2-small shapes (8192x3072x768,
 // 8192x768x3072, 8192x50304x768, 768x50304x8192): at K = 768 the epilogue
-// and output write cost as much as the MACs.
+// and output write cost as much as the MACs.  A persistent configuration with two
+// workgroups per CU runs twice as many at once (grid = 2 x CUs), each at about
+// half the MAC rate.
 struct TileCfg {
   int bm, bn, per_cu;
   double wg_macs;        // MAC/s of one resident workgroup in its main loop
@@ -1861,8 +1875,9 @@ static const TileCfg kCfgs[] = {
     {256, 128, 1, 3.0e12, 0, 6.0e-6, true, 64},   // persistent, 128x64 per wave (tests only)
     {128, 192, 1, 3.0e12, 0, 5.2e-6, true, 64},   // persistent, four waves, 64x96 each
     {128, 192, 1, 3.7e12, 0, 5.5e-6, true, 128},  // persistent, 128-byte stages, 64x96 per wave
+    {128, 128, 2, 1.75e12, 0, 4.5e-6, true, 128}, // the same, 64x64 per wave, two workgroups per CU
 };
-constexpr int kNumCfgs = 7;
+constexpr int kNumCfgs = 8;
 constexpr int kPersistStages = 4;
 
 // Compute units of the current device (cached per device).
@@ -1921,11 +1936,18 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
     if (t.persistent) {
       if (!allow_persistent || tiles > INT32_MAX / 2) continue;
       if (t.kstage == BK && (K % BK != 0 || kstages < kPersistStages - 1)) continue;
-      // 128-byte stages: at least one stage per 32x32 block of a wave (64x96
-      // wave tiles: 6), and no ragged tile-row
-      if (t.kstage == BK2 && (K % BK2 != 0 || K / BK2 < 6 || M % t.bm != 0)) continue;
+      // 128-byte stages: at least one stage per 32x32 block of a wave (2x2
+      // waves; 64x96 wave tiles: 6, 64x64: 4), and no ragged tile-row
+      const int wave_blocks = (t.bm / 64) * (t.bn / 64);
+      if (t.kstage == BK2 && (K % BK2 != 0 || K / BK2 < wave_blocks || M % t.bm != 0)) continue;
       if (force_splits > 1) continue;
-      const int64_t grid = tiles < cus ? tiles : cus;
+      const int64_t slots_p = (int64_t)cus * t.per_cu;
+      const int64_t grid = tiles < slots_p ? tiles : slots_p;
+      // two workgroups per CU measured faster only for short K and a few
+      // rounds of tiles (MLP up-projection 8192x3072x768: 35 against 38 us);
+      // slower on the LM head's 50 rounds at K = 768 (706 against ~680 us
+      // for tile 0) and its K = 8192 weight gradient (375 against ~355 us)
+      if (t.per_cu > 1 && (K > 1024 || tiles > 8 * grid)) continue;
       const double rounds = std::ceil((double)tiles / (double)grid);
       double cost = rounds * ((double)t.bm * t.bn * K / t.wg_macs + t.tile_overhead);
       const double wr = (double)M * N * 4 / write_bw;
@@ -2031,11 +2053,17 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
       else
         hipLaunchKernelGGL((gemm_i4_kernel<128, 128, 2, 2, false, true>), dim3(grid), dim3(256), 0, stream, p);
       break;
+    case 7:
+      if (p.relu)
+        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 128, 2, 2, true, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 128, 2, 2, false, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
+      break;
     default:
       if (p.relu)
-        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, true>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, true, 3, 1>), dim3(grid), dim3(256), 0, stream, p);
       else
-        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, false>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, false, 3, 1>), dim3(grid), dim3(256), 0, stream, p);
       break;
   }
   if (plan.splits > 1)

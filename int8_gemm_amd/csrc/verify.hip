@@ -296,7 +296,7 @@ const QCase kQCases[] = {{37, 301, false, 0, false},  {5, 4500, false, 0, false}
                          {33, 700, false, FMT_POW2, true}, {700, 33, true, 0, true}};
 const GCase kGCases[] = {{17, 33, 15, 0}, {130, 190, 70, 0}, {300, 520, 192, 0},
                          {256, 200, 768, 0}, {64, 64, 4096, 4}};
-constexpr int kGateCfgs = 7;   // tile configurations of the GEMM planner
+constexpr int kGateCfgs = 8;   // tile configurations of the GEMM planner
 constexpr size_t kGateWorkspace = 16u << 20;
 
 struct GateRun {

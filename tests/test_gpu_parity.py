@@ -229,25 +229,31 @@ def test_persistent_kernel(g, tile):
         os.environ.pop("I8G_FORCE_TILE", None)
 
 
-# 128-byte-stage persistent kernel: M % 128 == 0, K % 128 == 0, K >= 768.
-# Ragged N (masked through the buffer range check), one and several tiles per
-# workgroup, K with more stages than epilogue blocks (runtime stage loop).
+# 128-byte-stage persistent kernel: M % 128 == 0, K % 128 == 0, K / 128 at
+# least the 32x32 blocks of a wave (tile 6, 128x192: K >= 768; tile 7,
+# 128x128 with two workgroups per CU: K >= 512; shapes below the bound fall
+# back to another tile).  Ragged N (masked through the buffer range check),
+# one and several tiles per workgroup, K with more stages than epilogue blocks
+# (runtime stage loop), and for tile 7 K at its bound (four stages, two ring
+# slots) and more tiles than two per CU.
 PERSIST128_CASES = [(1024, 1000, 768, True), (4096, 1552, 768, False), (2048, 2000, 1536, True),
-                    (8192, 520, 896, False), (4224, 3000, 1280, True)]
+                    (8192, 520, 896, False), (4224, 3000, 1280, True), (2048, 1000, 512, True),
+                    (8192, 3000, 640, False)]
 
 
-def test_persistent128_kernel(g):
-    """The persistent kernel with 128-byte K stages against the oracle, every
+@pytest.mark.parametrize("tile", [6, 7])
+def test_persistent128_kernel(g, tile):
+    """The persistent kernels with 128-byte K stages against the oracle, every
     byte and the hash."""
-    rng = np.random.default_rng(96)
+    rng = np.random.default_rng(96 + tile)
     try:
-        os.environ["I8G_FORCE_TILE"] = "6"
+        os.environ["I8G_FORCE_TILE"] = str(tile)
         for (m, n, k, relu) in PERSIST128_CASES:
             A = rng.standard_t(3, (m, k)).astype(F32)
             B = rng.standard_normal((k, n)).astype(F32)
             A[rng.random(m) < 0.02] = 0
             B[:, rng.random(n) < 0.02] = 0
-            say("persistent128 MNK", m, n, k, "relu", relu)
+            say("persistent128 tile", tile, "MNK", m, n, k, "relu", relu)
             got = run_method(g, A, B, relu=relu)
             check_against_oracle(got, A, B, relu)
     finally:
