@@ -26,6 +26,7 @@ operand write those codes and scales itself (gemm_i8_requant).
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -301,17 +302,25 @@ def cpu_baseline(tensors, gemms, ops, budget_s=10.0, fmt_b=0):
 # ---------------------------------------------------------------------------
 # traffic from committed PMC summaries (null unless the kernels are unchanged)
 # ---------------------------------------------------------------------------
+def code_digest_text(text):
+    """Source text without comments and with whitespace collapsed: edits to
+    comments or layout leave the digest unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha():
-    """Digest of the sources the timed kernels and their planner are built
+    """Digest of the code the timed kernels and their planner are built
     from (api.hip holds the host-side argument checks and verify.hip the
-    self-checks; neither changes a kernel)."""
+    self-checks; neither changes a kernel).  Comments do not count."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int8_gemm_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f in ("verify.hip", "api.hip"):
             continue
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + code_digest_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

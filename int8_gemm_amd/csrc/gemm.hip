@@ -1549,10 +1549,11 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // If DRAIN, block BLK of Y (tile r-1, Out oy) is drained: parts 0-1 with
   // the operand half `early` (read during the previous stage), parts 2-3 with
   // `late`, which mid() reads just before the barrier together with the next
-  // stage's early half.  ST: the stage's loads are waited for with this many
-  // later stores allowed outstanding (a lower bound of the stores issued
-  // after them: those of k-step 3 of the previous stage and of k-steps 0-1 of
-  // this one, counted only where those stages drain).
+  // stage's early half.  ST: stage g+1's loads are waited for with this many
+  // later memory operations allowed outstanding, a lower bound of those
+  // issued after them: the loads of the STAGES-2 stages issued since, the
+  // previous stage's stores that follow them (PREV_ST) and the stores of
+  // k-steps 0-2 of this one, stores counted only where those stages drain.
   auto stage = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int g, const Out& oy, const DHalf& early,
                    int scb, DHalf& late, auto FIRST, auto DRAIN, auto BLK, auto STV, auto&& mid)
       __attribute__((always_inline)) {
