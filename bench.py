@@ -14,8 +14,8 @@ synthetic f32 tensors, resident in HBM before timing starts.
 
 Prints ONE JSON line: value = int8 GEMM operations (2MNK summed over the
 step's GEMMs) per second of the whole step, in TOPS, from HIP events around
-K steps, each step one replay of the step captured in a HIP graph (--eager:
-launched call by call); `roofline` for the step's dominant kernel, whose
+K steps, replays of HIP graphs that hold ten steps each (--steps-per-graph;
+--eager: launched call by call); `roofline` for the step's dominant kernel, whose
 device duration is timed with HIP events around a batch of back-to-back
 launches of that call; `cpu_baseline` = the CPU oracle timed on this host;
 `parity` = whether the oracle's output hashes equal the GPU's.
@@ -349,6 +349,9 @@ def main():
                     help="a GEMM whose output feeds the next GEMM's per-row quantize writes int8 "
                          "codes and scales directly (gemm_i8_requant; the f32 output is not stored)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steps-per-graph", type=int, default=10, metavar="S",
+                    help="steps captured in one HIP graph; the K timed steps are K // S replays of "
+                         "it and K % S replays of a one-step graph")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the step captured in a HIP graph")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
@@ -387,39 +390,57 @@ def main():
     # only kernels on the given stream and leaves its workspace header zero, so
     # a replay repeats the step exactly).  Every replay of the check below,
     # with eager steps between them, must reproduce the eager hashes.
-    graph = None
+    # Several steps go into one graph (--steps-per-graph): with one step per
+    # graph the kernel trace shows the GPU idle ~8 us between consecutive
+    # replays, none between the kernels inside one.
+    graph = graph_s = None
+    spg = max(1, a.steps_per_graph)
     if not a.eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step.run()
         torch.cuda.synchronize()
-        for _ in range(3):
-            for e in step.gemms:
-                e["h"].zero_()
-            graph.replay()
+        graphs = [graph]
+        if spg > 1 and a.steps >= spg:
+            graph_s = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph_s):
+                for _ in range(spg):
+                    step.run()
             torch.cuda.synchronize()
-            if step.hashes() != gpu_hashes:
-                raise SystemExit("graph replay changed the output hashes")
-            step.run()
-            torch.cuda.synchronize()
-            if step.hashes() != gpu_hashes:
-                raise SystemExit("eager step after a replay changed the output hashes")
+            graphs.append(graph_s)
+        for gr in graphs:
+            for _ in range(3):
+                for e in step.gemms:
+                    e["h"].zero_()
+                gr.replay()
+                torch.cuda.synchronize()
+                if step.hashes() != gpu_hashes:
+                    raise SystemExit("graph replay changed the output hashes")
+                step.run()
+                torch.cuda.synchronize()
+                if step.hashes() != gpu_hashes:
+                    raise SystemExit("eager step after a replay changed the output hashes")
         for _ in range(a.warmup):
             graph.replay()
         torch.cuda.synchronize()
 
     # timed region: exactly K steps (graph replays, or eager launches)
-    log(f"[bench] timing {a.steps} steps ({'eager' if graph is None else 'graph replay'})")
+    n_s = a.steps // spg if graph_s is not None else 0
+    n_1 = a.steps - n_s * spg
+    log(f"[bench] timing {a.steps} steps ({'eager' if graph is None else f'{n_s} replays of a {spg}-step graph, {n_1} of a one-step graph'})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     start.record(stream)
-    for _ in range(a.steps):
-        if graph is None:
+    if graph is None:
+        for _ in range(a.steps):
             step.run()
-        else:
+    else:
+        for _ in range(n_s):
+            graph_s.replay()
+        for _ in range(n_1):
             graph.replay()
     stop.record(stream)
     torch.cuda.synchronize()
@@ -542,7 +563,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "gpu_hashes": [f"{h:#018x}" for h in gpu_hashes],
-        "launch": "eager" if graph is None else "hip graph replay per step",
+        "launch": ("eager" if graph is None else
+                   f"hip graph replays ({n_s} x {spg} steps + {n_1} x 1 step)"),
     }
     print(json.dumps(out), flush=True)
 
