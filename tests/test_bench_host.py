@@ -1,6 +1,5 @@
 """Host-side logic of bench.py (no GPU): the kernel-code digest that decides
-whether the stored HBM traffic counters still describe the kernels, and the
-split of the timed steps over multi-step graphs."""
+whether the stored HBM traffic counters still describe the kernels."""
 import os
 import sys
 
