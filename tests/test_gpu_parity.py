@@ -319,23 +319,31 @@ def test_max_k_int32_limit(g, splits):
     assert g.hash_value(h) == hashref.output_hash(want)
 
 
-@pytest.mark.parametrize("case", [(256, 200, 768, 333), (300, 70, 200, 80), (3, 64, 128, (1 << 23) + 64)])
+@pytest.mark.parametrize("case", [(256, 200, 768, 333, None), (256, 200, 768, 333, 6),
+                                  (256, 200, 768, 333, 7), (300, 70, 200, 80, None),
+                                  (3, 64, 128, (1 << 23) + 64, None)])
 def test_output_leading_dimension(g, case):
     """C written through a row stride larger than N: the cells of C match
     the oracle, the columns between N and ldc keep their contents, and the
     hash covers C only.  A stride above 2^23 floats takes the non-persistent
-    kernels (the persistent ones address C with 32-bit offsets)."""
-    M, N, K, ldc = case
+    kernels (the persistent ones address C with 32-bit offsets); the 256-row
+    case also runs on both 128-byte-stage persistent tiles (6 and 7)."""
+    M, N, K, ldc, tile = case
     rng = np.random.default_rng(M + N + K)
     A = rng.standard_normal((M, K)).astype(F32)
     B = rng.standard_normal((K, N)).astype(F32)
     want, QA, sA, QB, sB = ref.blockscaled_gemm(A, B, relu=True)
-    say("ldc", M, N, K, ldc)
+    say("ldc", M, N, K, ldc, "tile", tile)
     dQA, dsA = g.quantize_rows(torch.from_numpy(A).cuda())
     dQB, dsB = g.quantize_cols(torch.from_numpy(B).cuda())
     buf = torch.full((M, ldc), -7.25, dtype=torch.float32, device="cuda")
-    C, h = g.gemm_i8_blockscaled(dQA, dsA, dQB, dsB, relu=True, want_hash=True, out=buf[:, :N])
-    torch.cuda.synchronize()
+    if tile is not None:
+        os.environ["I8G_FORCE_TILE"] = str(tile)
+    try:
+        C, h = g.gemm_i8_blockscaled(dQA, dsA, dQB, dsB, relu=True, want_hash=True, out=buf[:, :N])
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("I8G_FORCE_TILE", None)
     got = buf[:, :N].cpu().numpy()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     pad = buf[:, N:min(ldc, N + 4096)]
