@@ -161,6 +161,29 @@ def test_whole_method_int4_weights_mlp_down(g, int4_path):
         assert g.hash_value(h) == hashref.output_hash(C_ref)
 
 
+@pytest.mark.parametrize("tile", [6, 7])
+def test_int4_weights_on_persistent_tiles(g, tile):
+    """int4 weights widened to int8 codes and multiplied by each 128-byte-stage
+    persistent tile (forced), up-projection shape with 1024 tokens, ragged N
+    and ReLU: bit for bit against the oracle."""
+    M, K, N = 1024, 768, 1000
+    rng = np.random.default_rng(40 + tile)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    C_ref, QA, sr, QB, sc = F.blockscaled_gemm(A, B, 0, F.INT4, relu=True)
+    dA, dsr = g.quantize_rows(torch.from_numpy(A).cuda())
+    dB, dsc = g.quantize_cols_fmt(torch.from_numpy(B).cuda(), F.INT4)
+    say("int4 weights tile", tile)
+    os.environ["I8G_FORCE_TILE"] = str(tile)
+    try:
+        C, h = g.gemm_i8_blockscaled(dA, dsr, dB, dsc, relu=True, want_hash=True, K=K, b_int4=True)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("I8G_FORCE_TILE", None)
+    assert np.array_equal(C.cpu().numpy().view(np.uint32), C_ref.view(np.uint32))
+    assert g.hash_value(h) == hashref.output_hash(C_ref)
+
+
 def test_format_argument_errors(g):
     lib = g.load()
     X = torch.zeros((4, 40), dtype=torch.float32, device="cuda")
