@@ -1661,7 +1661,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     tile_coords(0, tm, tn);
     make_src(0, tm, tn, fsrc);
     make_out(0, tm, tn, out_cur);
-    // prologue: scales and the first three stages of tile 0
+    // prologue: scales and the first STAGES stages of tile 0
     issue_scales(fsrc);
     static_for<0, STAGES>([&](auto SI) __attribute__((always_inline)) {
       issue_ops(decltype(SI)::value, fsrc, decltype(SI)::value);
