@@ -15,10 +15,16 @@ synthetic f32 tensors, resident in HBM before timing starts.
 Prints ONE JSON line: value = int8 GEMM operations (2MNK summed over the
 step's GEMMs) per second of the whole step, in TOPS, from HIP events around
 K steps, replays of HIP graphs that hold ten steps each (--steps-per-graph;
---eager: launched call by call); `roofline` for the step's dominant kernel, whose
-device duration is timed with HIP events around a batch of back-to-back
-launches of that call; `cpu_baseline` = the CPU oracle timed on this host;
-`parity` = whether the oracle's output hashes equal the GPU's.
+--eager: launched call by call); `kernels` = every call of the step with its
+device duration (HIP events around a batch of back-to-back launches: warm)
+and, unless --no-cold, its duration when a 512 MiB scrub write precedes each
+launch (cold: inputs evicted from the 256 MB last-level cache); `roofline`
+for the step's dominant kernel; `lm_head` (MLP workload only, unless
+--no-head) = the LM-head GEMMs measured in the same run (forward
+8192x50304x768, weight gradient 768x50304x8192: per-GEMM durations, TOPS,
+roofline fractions, warm and cold); `cpu_baseline` = the CPU oracle timed on
+this host; `parity` = whether output_hash of every stored output, read back
+from device memory, equals the oracle's hash (and the fused hash).
 --b-format stores every B operand in one of the presk page's "Integer
 weights" formats (the headline line uses the default int8 / absmax).
 --requant lets a GEMM whose output is the next GEMM's per-row quantized
@@ -237,7 +243,20 @@ class GpuStep:
                 fn()
 
     def hashes(self):
+        """The hashes the GEMM kernels fused into their epilogues."""
         return [self.g.hash_value(e["h"]) for e in self.gemms]
+
+    def stored_hashes(self):
+        """output_hash of every stored output, read back from device memory
+        (None for a requantized output, which is not stored)."""
+        out = []
+        for e in self.gemms:
+            if e["requant_into"] is not None:
+                out.append(None)
+                continue
+            out.append(self.g.hash_value(self.g.output_hash(e["C"])))
+        self.torch.cuda.synchronize()
+        return out
 
 
 # ---------------------------------------------------------------------------
@@ -278,12 +297,14 @@ def cpu_baseline(tensors, gemms, ops, budget_s=10.0, fmt_b=0):
     from threadpoolctl import threadpool_info
     blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
     threads = max([d.get("num_threads", 1) for d in blas] or [1])
+    host = {"cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "blas_threads": threads}
     t0 = time.perf_counter()
     hashes, done = oracle_step(tensors, gemms, budget_s, fmt_b)
     first = time.perf_counter() - t0
     if len(hashes) < len(gemms):
         return {"value": done / first / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-                "sample": f"the first {len(hashes)} of the step's {len(gemms)} GEMMs "
+                **host, "sample": f"the first {len(hashes)} of the step's {len(gemms)} GEMMs "
                           f"({done / 1e9:.1f} GOP) in {first:.1f} s; numpy float32 per-op "
                           f"quantize/epilogue (1 thread), float64 BLAS contraction "
                           f"({threads} threads), numpy uint64 hash"}, hashes
@@ -293,7 +314,7 @@ def cpu_baseline(tensors, gemms, ops, budget_s=10.0, fmt_b=0):
         oracle_step(tensors, gemms, None, fmt_b)
         times.append(time.perf_counter() - t1)
     sec = statistics.median(times)
-    return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+    return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle", **host,
             "sample": f"{len(times)} full step(s) of the same workload, median {sec:.2f} s; "
                       f"numpy float32 per-op quantize/epilogue (1 thread), float64 BLAS "
                       f"contraction ({threads} threads), numpy uint64 hash"}, hashes
@@ -336,6 +357,236 @@ def traffic_for(kernel_key):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def capture_graphs(torch, step, steps, spg, ref_hashes):
+    """HIP graphs of one step and (when at least spg steps are timed) of spg
+    steps.  The library allocates nothing, launches only kernels on the given
+    stream and leaves its workspace header zero, so a replay repeats the step
+    exactly; every replay below, with eager steps between them, must
+    reproduce the eager hashes.  With one step per graph the kernel trace
+    shows the GPU idle ~8 us between consecutive replays, none between the
+    kernels inside one: hence several steps per graph."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run()
+    torch.cuda.synchronize()
+    graphs, graph_s = [graph], None
+    if spg > 1 and steps >= spg:
+        graph_s = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_s):
+            for _ in range(spg):
+                step.run()
+        torch.cuda.synchronize()
+        graphs.append(graph_s)
+    for gr in graphs:
+        for _ in range(3):
+            for e in step.gemms:
+                e["h"].zero_()
+            gr.replay()
+            torch.cuda.synchronize()
+            if step.hashes() != ref_hashes:
+                raise SystemExit("graph replay changed the output hashes")
+            step.run()
+            torch.cuda.synchronize()
+            if step.hashes() != ref_hashes:
+                raise SystemExit("eager step after a replay changed the output hashes")
+    return graph, graph_s
+
+
+def time_steps(torch, step, steps, warmup, spg, eager, ref_hashes):
+    """Device time of exactly `steps` steps (HIP events on the step's
+    stream), as graph replays or eager launches.  Returns (ms per step,
+    wall ms per step, launch description)."""
+    graph = graph_s = None
+    if not eager:
+        graph, graph_s = capture_graphs(torch, step, steps, spg, ref_hashes)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    n_s = steps // spg if graph_s is not None else 0
+    n_1 = steps - n_s * spg
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    start.record(stream)
+    if graph is None:
+        for _ in range(steps):
+            step.run()
+    else:
+        for _ in range(n_s):
+            graph_s.replay()
+        for _ in range(n_1):
+            graph.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if step.hashes() != ref_hashes:
+        raise SystemExit("timed steps changed the output hashes")
+    launch = "eager" if graph is None else f"hip graph replays ({n_s} x {spg} steps + {n_1} x 1 step)"
+    return start.elapsed_time(stop) / steps, wall * 1e3 / steps, launch
+
+
+def time_call(torch, step, fn, reps, scrub=None):
+    """Average device time of one call in microseconds.
+    Warm (scrub is None): the call launched `reps` times back to back on the
+    step's stream, behind a short sleep kernel so that the host runs ahead of
+    the GPU, one event pair around the batch; its inputs stay in the caches.
+    Cold: before each launch the 512 MiB `scrub` buffer is overwritten (more
+    than the 256 MB last-level cache), so the call starts from HBM; each
+    launch has its own event pair."""
+    torch.cuda.synchronize()
+    if scrub is None:
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(2_000_000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(step.stream)
+        for _ in range(reps):
+            fn()
+        e1.record(step.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    ev = []
+    for r in range(reps):
+        scrub.fill_(r & 0x7F)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(step.stream)
+        fn()
+        e1.record(step.stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return statistics.mean(a.elapsed_time(b) for a, b in ev) * 1e3
+
+
+def call_record(step, e, label, avg, cold, fmt_b):
+    """Algorithmic bytes / ops of one call of the step and its rates."""
+    M, N, K = e["M"], e["N"], e["K"]
+    if label in ("gemm", "requant"):
+        gops = 2.0 * M * N * K
+        b_bytes = N * int4_line_bytes(K) if fmt_b & 2 else N * K
+        out_bytes = 4 * M * N if label == "gemm" else M * N + 4 * M   # f32, or int8 + scales
+        nbytes = M * K + b_bytes + 4 * M + 4 * N + out_bytes + 8
+        bound = "mfma" if gops / nbytes >= RIDGE else "hbm"
+        shape = f"{M}x{N}x{K}"
+    else:
+        # the quantized source tensor and the direction of its scales
+        mode = e["a_mode"] if label == "quantize_A" else e["b_mode"]
+        rows, cols = step.t[e["a_key"] if label == "quantize_A" else e["b_key"]].shape
+        nscale = rows if mode == "rows" else cols
+        nlines, length = (rows, cols) if mode == "rows" else (cols, rows)
+        qbytes = nlines * int4_line_bytes(length) if (label == "quantize_B" and fmt_b & 2) else rows * cols
+        gops, nbytes, bound = 0.0, 4 * rows * cols + qbytes + 4 * nscale, "hbm"
+        shape = f"{rows}x{cols} ({mode})"
+
+    def rate(us):
+        if bound == "mfma":
+            return gops / (us * 1e-6) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
+        return nbytes / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s"
+
+    ach, peak, unit = rate(avg)
+    rec = {"call": f"{e['name']}.{label}", "shape": shape, "avg_us": round(avg, 2),
+           "total_us_per_step": round(avg, 2), "bound": bound,
+           "achieved": round(ach, 1), "peak": peak, "unit": unit,
+           "frac": round(ach / peak, 4), "algorithmic_bytes": nbytes, "int8_ops": gops,
+           "tops": round(gops / (avg * 1e-6) / 1e12, 1) if gops else None}
+    if gops:
+        rec["pct_of_int8_peak"] = round(100.0 * gops / (avg * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
+    if cold is not None:
+        cach, _, _ = rate(cold)
+        rec["cold_avg_us"] = round(cold, 2)
+        rec["cold_frac"] = round(cach / peak, 4)
+        if gops:
+            rec["cold_tops"] = round(gops / (cold * 1e-6) / 1e12, 1)
+    return rec
+
+
+def measure_calls(torch, step, reps, cold_reps, scrub, fmt_b):
+    """Per-call device durations (warm, and cold when scrub is given) of
+    every call of the step, and of the batched input passes as the step
+    issues them.  Returns (records, batch record or None)."""
+    kernels = []
+    for e in step.gemms:
+        for label, fn in step.calls(e):
+            avg = time_call(torch, step, fn, reps)
+            cold = time_call(torch, step, fn, cold_reps, scrub) if scrub is not None else None
+            kernels.append(call_record(step, e, label, avg, cold, fmt_b))
+    batch = None
+    if step.njobs:
+        # the batch runs the input passes timed one by one above; its bytes
+        # are theirs (it is not a single kernel, so it is not a roofline candidate)
+        us = time_call(torch, step, step._batch, reps)
+        cold = time_call(torch, step, step._batch, cold_reps, scrub) if scrub is not None else None
+        parts = [k for k in kernels if tuple(k["call"].rsplit(".", 1)) in set(step.batched)]
+        nbytes = sum(k["algorithmic_bytes"] for k in parts)
+        batch = {"call": "inputs.quantize_batch", "passes": len(parts), "avg_us": round(us, 2),
+                 "sum_of_single_calls_us": round(sum(k["avg_us"] for k in parts), 2),
+                 "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                 "algorithmic_bytes": nbytes}
+        if cold is not None:
+            batch["cold_avg_us"] = round(cold, 2)
+            batch["cold_achieved"] = round(nbytes / (cold * 1e-6) / 1e9, 1)
+    return kernels, batch
+
+
+def golden_head_hashes():
+    """The oracle's output hashes of the LM-head GEMMs (forward, weight
+    gradient), written by tests/golden/make_step_golden.py from oracle/."""
+    path = os.path.join(ROOT, "tests", "golden", "step_golden.json")
+    with open(path) as f:
+        gh = json.load(f)["head"]
+    return [int(gh["fwd"]["hash"], 16), int(gh["wgrad"]["hash"], 16)]
+
+
+def lm_head_record(g, torch, args, scrub):
+    """The LM-head GEMMs (forward 8192x50304x768, weight gradient
+    768x50304x8192) measured in the same run as the headline: the whole
+    LM-head step (its quantize passes and both GEMMs), and per call warm and
+    cold durations with TOPS and roofline fractions.  Parity: output_hash of
+    the stored outputs against the oracle's hashes."""
+    desc, tensors, gemms = make_workload("head")
+    step = GpuStep(g, torch, tensors, gemms)
+    del tensors
+    step.run()
+    torch.cuda.synchronize()
+    fused = step.hashes()
+    stored = step.stored_hashes()
+    want = golden_head_hashes()
+    steps = max(2, min(args.steps, 10))
+    ms, _, launch = time_steps(torch, step, steps, 1, max(1, min(args.steps_per_graph, steps)), args.eager, fused)
+    reps = max(3, min(args.steps, 10))
+    kernels, batch = measure_calls(torch, step, reps, 3, scrub, 0)
+    if step.hashes() != fused:
+        raise SystemExit("LM head: repeated calls changed the output hashes")
+    ops = sum(2.0 * e["M"] * e["N"] * e["K"] for e in step.gemms)
+    rec = {"workload": desc, "steps": steps, "ms_per_step": round(ms, 4),
+           "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+           "pct_of_int8_peak": round(100.0 * ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+           "launch": launch,
+           "gemms": [k for k in kernels if k["call"].endswith(".gemm")],
+           "quantize": [k for k in kernels if not k["call"].endswith(".gemm")],
+           "quantize_batch": batch,
+           "parity": stored == want and fused == want,
+           "gpu_hashes": [f"{h:#018x}" for h in stored]}
+    del step
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +600,10 @@ def main():
                     help="a GEMM whose output feeds the next GEMM's per-row quantize writes int8 "
                          "codes and scales directly (gemm_i8_requant; the f32 output is not stored)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-head", action="store_true",
+                    help="leave out the LM-head sub-record of the MLP workload's line")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="leave out the cold-cache (512 MiB scrub before each launch) timings")
     ap.add_argument("--steps-per-graph", type=int, default=10, metavar="S",
                     help="steps captured in one HIP graph; the K timed steps are K // S replays of "
                          "it and K % S replays of a one-step graph")
@@ -363,7 +618,6 @@ def main():
               "(its sharding is described in DESIGN.md); rerun with --gpus 1", flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import int8_gemm_amd as g
 
@@ -386,157 +640,45 @@ def main():
     torch.cuda.synchronize()
     gpu_hashes = step.hashes()
 
-    # One step captured in a HIP graph (the library allocates nothing, launches
-    # only kernels on the given stream and leaves its workspace header zero, so
-    # a replay repeats the step exactly).  Every replay of the check below,
-    # with eager steps between them, must reproduce the eager hashes.
-    # Several steps go into one graph (--steps-per-graph): with one step per
-    # graph the kernel trace shows the GPU idle ~8 us between consecutive
-    # replays, none between the kernels inside one.
-    graph = graph_s = None
-    spg = max(1, a.steps_per_graph)
-    if not a.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step.run()
-        torch.cuda.synchronize()
-        graphs = [graph]
-        if spg > 1 and a.steps >= spg:
-            graph_s = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph_s):
-                for _ in range(spg):
-                    step.run()
-            torch.cuda.synchronize()
-            graphs.append(graph_s)
-        for gr in graphs:
-            for _ in range(3):
-                for e in step.gemms:
-                    e["h"].zero_()
-                gr.replay()
-                torch.cuda.synchronize()
-                if step.hashes() != gpu_hashes:
-                    raise SystemExit("graph replay changed the output hashes")
-                step.run()
-                torch.cuda.synchronize()
-                if step.hashes() != gpu_hashes:
-                    raise SystemExit("eager step after a replay changed the output hashes")
-        for _ in range(a.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-
     # timed region: exactly K steps (graph replays, or eager launches)
-    n_s = a.steps // spg if graph_s is not None else 0
-    n_1 = a.steps - n_s * spg
-    log(f"[bench] timing {a.steps} steps ({'eager' if graph is None else f'{n_s} replays of a {spg}-step graph, {n_1} of a one-step graph'})")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream()
-    start.record(stream)
-    if graph is None:
-        for _ in range(a.steps):
-            step.run()
-    else:
-        for _ in range(n_s):
-            graph_s.replay()
-        for _ in range(n_1):
-            graph.replay()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop)
-    ms_per_step = gpu_ms / a.steps
+    spg = max(1, a.steps_per_graph)
+    log(f"[bench] timing {a.steps} steps")
+    ms_per_step, wall_ms, launch = time_steps(torch, step, a.steps, a.warmup, spg, a.eager, gpu_hashes)
     value = ops / (ms_per_step * 1e-3) / 1e12
-    log(f"[bench] {ms_per_step:.4f} ms/step (wall {wall / a.steps * 1e3:.4f} ms/step), {value:.1f} TOPS")
-    if step.hashes() != gpu_hashes:
-        raise SystemExit("timed steps changed the output hashes")
+    log(f"[bench] {ms_per_step:.4f} ms/step (wall {wall_ms:.4f} ms/step, {launch}), {value:.1f} TOPS")
 
-    # Per-call device durations: every call of the step launched R times back
-    # to back on the same stream, behind a short sleep kernel so that the host
-    # runs ahead of the GPU, with one event pair around the R launches.
-    per = {}
+    # per-call device durations, warm and cold
+    scrub = None if a.no_cold else torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     reps = max(5, min(a.steps, 50))
-    for e in step.gemms:
-        for label, fn in step.calls(e):
-            torch.cuda.synchronize()
-            if hasattr(torch.cuda, "_sleep"):
-                torch.cuda._sleep(2_000_000)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(step.stream)
-            for _ in range(reps):
-                fn()
-            e1.record(step.stream)
-            torch.cuda.synchronize()
-            per[(e["name"], label)] = [e0.elapsed_time(e1) * 1e3 / reps]
-    batch_us = None
-    if step.njobs:
-        # the batched input passes as the step issues them (one call)
-        torch.cuda.synchronize()
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(2_000_000)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(step.stream)
-        for _ in range(reps):
-            step._batch()
-        e1.record(step.stream)
-        torch.cuda.synchronize()
-        batch_us = e0.elapsed_time(e1) * 1e3 / reps
+    kernels, batch_entry = measure_calls(torch, step, reps, max(3, min(a.steps, 20)), scrub, fmt_b)
     if step.hashes() != gpu_hashes:
         raise SystemExit("repeated calls changed the output hashes")
-    kernels = []
-    for (name, label), us in per.items():
-        e = next(x for x in step.gemms if x["name"] == name)
-        avg = statistics.mean(us)
-        M, N, K = e["M"], e["N"], e["K"]
-        if label in ("gemm", "requant"):
-            gops = 2.0 * M * N * K
-            b_bytes = N * int4_line_bytes(K) if fmt_b & 2 else N * K
-            out_bytes = 4 * M * N if label == "gemm" else M * N + 4 * M   # f32, or int8 + scales
-            nbytes = M * K + b_bytes + 4 * M + 4 * N + out_bytes + 8
-            bound = "mfma" if gops / nbytes >= RIDGE else "hbm"
-            shape = f"{M}x{N}x{K}"
-        else:
-            # the quantized source tensor and the direction of its scales
-            mode = e["a_mode"] if label == "quantize_A" else e["b_mode"]
-            rows, cols = step.t[e["a_key"] if label == "quantize_A" else e["b_key"]].shape
-            nscale = rows if mode == "rows" else cols
-            nlines, length = (rows, cols) if mode == "rows" else (cols, rows)
-            qbytes = nlines * int4_line_bytes(length) if (label == "quantize_B" and fmt_b & 2) else rows * cols
-            gops, nbytes, bound = 0.0, 4 * rows * cols + qbytes + 4 * nscale, "hbm"
-            shape = f"{rows}x{cols} ({mode})"
-        if bound == "mfma":
-            ach, peak, unit = gops / (avg * 1e-6) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
-        else:
-            ach, peak, unit = nbytes / (avg * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s"
-        kernels.append({"call": f"{name}.{label}", "shape": shape, "avg_us": round(avg, 2),
-                        "total_us_per_step": round(avg, 2), "bound": bound,
-                        "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                        "frac": round(ach / peak, 4), "algorithmic_bytes": nbytes,
-                        "int8_ops": gops,
-                        "tops": round(gops / (avg * 1e-6) / 1e12, 1) if gops else None})
-    if batch_us is not None:
-        # the batch runs the input passes timed one by one above; its bytes
-        # are theirs (it is not a single kernel, so it is not a roofline candidate)
-        parts = [k for k in kernels if tuple(k["call"].rsplit(".", 1)) in set(step.batched)]
-        nbytes = sum(k["algorithmic_bytes"] for k in parts)
-        batch_entry = {"call": "inputs.quantize_batch", "passes": len(parts), "avg_us": round(batch_us, 2),
-                       "sum_of_single_calls_us": round(sum(k["avg_us"] for k in parts), 2),
-                       "achieved": round(nbytes / (batch_us * 1e-6) / 1e9, 1), "unit": "GB/s",
-                       "algorithmic_bytes": nbytes}
+    # parity is judged on the stored outputs: output_hash reads every output
+    # back from device memory (outside the timed region)
+    stored_hashes = step.stored_hashes()
     dom = max(kernels, key=lambda k: k["avg_us"])
     roof = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
             "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic_for(dom["call"]),
             "kernel": dom["call"], "shape": dom["shape"], "avg_us": dom["avg_us"]}
+    if "cold_avg_us" in dom:
+        roof["cold_avg_us"] = dom["cold_avg_us"]
+        roof["cold_frac"] = dom["cold_frac"]
+
+    head = None
+    if a.workload == "mlp" and not a.no_head and fmt_b == 0 and not a.requant:
+        log("[bench] LM-head GEMMs (sub-record)")
+        head = lm_head_record(g, torch, a, scrub)
+        log(f"[bench] LM head {head['ms_per_step']:.3f} ms/step, {head['tops']:.1f} TOPS, parity {head['parity']}")
+    del scrub
 
     cpu = None
     parity = None
     if not a.no_cpu_baseline:
         log("[bench] cpu_baseline: oracle on the host")
         cpu, cpu_hashes = cpu_baseline(tensors, gemms, ops, fmt_b=fmt_b)
-        parity = cpu_hashes == gpu_hashes[:len(cpu_hashes)]
+        n = len(cpu_hashes)
+        parity = (cpu_hashes == stored_hashes[:n] and
+                  all(s is None or s == f for s, f in zip(stored_hashes, gpu_hashes)))
         log(f"[bench] oracle {cpu['value']:.4f} TOPS, parity {parity}")
 
     out = {
@@ -559,12 +701,14 @@ def main():
         "pct_of_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
         "roofline": roof,
         "kernels": kernels,
-        "quantize_batch": batch_entry if batch_us is not None else None,
+        "quantize_batch": batch_entry,
+        "lm_head": head,
         "cpu_baseline": cpu,
         "parity": parity,
+        "parity_basis": "output_hash of every stored output (read back from device memory) "
+                        "against the CPU oracle's hashes, plus the fused hashes equal to those",
         "gpu_hashes": [f"{h:#018x}" for h in gpu_hashes],
-        "launch": ("eager" if graph is None else
-                   f"hip graph replays ({n_s} x {spg} steps + {n_1} x 1 step)"),
+        "launch": launch,
     }
     print(json.dumps(out), flush=True)
 
