@@ -377,6 +377,38 @@ size_t i8g_probe_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int i8g_probe_hash(uint64_t seed, int64_t M, int64_t N, int64_t K, uint64_t* hash,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Test hooks.  The bytes a call writes never depend on the kernel plan (the
+ * contraction is exact in any blocking and K split); these two calls let a
+ * test run every kernel path on shapes the planner would not give it and
+ * check which plan ran.  Not for production use.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * i8g_set_test_overrides -- process-wide plan overrides for the calls that
+ * follow (all devices, all threads; a call racing with it sees either
+ * setting).  force_tile: -1 = the planner's choice, else a tile
+ * configuration index 0..7 (a configuration that cannot run a shape falls
+ * back to the 128x128 tile, index 2); force_splits: 0 = the planner's
+ * choice, else the number of K splits (clamped so that no split is empty;
+ * the persistent configurations never split); qcols_two_pass: 1 = column
+ * quantize passes through the two-pass kernels; int4_direct: 1 = int4 GEMM
+ * operands read packed by the direct int4 kernel.  All zero / -1 restores
+ * the default.  Errors: I8G_EINVAL for out-of-range values.
+ */
+int i8g_set_test_overrides(int32_t force_tile, int32_t force_splits, int32_t qcols_two_pass,
+                           int32_t int4_direct);
+
+/*
+ * i8g_plan_query -- the plan gemm_i8_blockscaled would use for this shape on
+ * the current device under the current overrides: *config = tile
+ * configuration index (8 = the direct int4 kernel), *splits = K splits.
+ * Host only; enqueues nothing.  Errors: I8G_EINVAL (M or N < 1, K < 0,
+ * ldc < N, null outputs, unknown flags).
+ */
+int i8g_plan_query(int64_t M, int64_t N, int64_t K, int64_t ldc, uint32_t flags, int32_t* config,
+                   int32_t* splits);
+
 /* Static English text for a status code (never NULL). */
 const char* i8g_status_string(int status);
 

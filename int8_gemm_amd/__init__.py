@@ -18,6 +18,7 @@ Hash tensors hold the 64-bit hash in an int64 element; ``hash_value``
 returns it as a Python int in [0, 2^64).  If the library is not built, or
 cannot be loaded, every entry point raises: there is no fallback.
 """
+import contextlib
 import ctypes
 import os
 
@@ -42,7 +43,8 @@ EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_wo
             "i8g_gate", "i8g_gate_workspace_bytes", "i8g_audit_gemm", "i8g_audit_quantize",
             "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt",
             "gemm_i8_requant", "gemm_i8_requant_workspace_bytes", "quantize_batch",
-            "gemm_i8_workspace_bytes_flags", "i8g_audit_quantize_fmt")
+            "gemm_i8_workspace_bytes_flags", "i8g_audit_quantize_fmt", "i8g_set_test_overrides",
+            "i8g_plan_query")
 
 _lib = None
 _ws = {}
@@ -115,6 +117,12 @@ def load():
     lib.i8g_probe_workspace_bytes.restype = c_sz
     lib.i8g_probe_hash.argtypes = [ctypes.c_uint64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
     lib.i8g_probe_hash.restype = ctypes.c_int
+    c_i32 = ctypes.c_int32
+    lib.i8g_set_test_overrides.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    lib.i8g_set_test_overrides.restype = ctypes.c_int
+    lib.i8g_plan_query.argtypes = [c_i64, c_i64, c_i64, c_i64, c_u32, ctypes.POINTER(c_i32),
+                                   ctypes.POINTER(c_i32)]
+    lib.i8g_plan_query.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -401,6 +409,42 @@ def probe_hash(seed, M, N, K, device=None):
         _check(lib.i8g_probe_hash(seed & ((1 << 64) - 1), M, N, K, _ptr(h), ctypes.c_void_p(ws.data_ptr()),
                                   nbytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
     return h
+
+
+_overrides = {"force_tile": -1, "force_splits": 0, "qcols_two_pass": 0, "int4_direct": 0}
+
+
+@contextlib.contextmanager
+def plan_overrides(**kw):
+    """Plan overrides for tests (i8g_set_test_overrides) inside a with-block:
+    force_tile (-1: the planner's choice), force_splits (0: the planner's),
+    qcols_two_pass, int4_direct.  Blocks nest: settings not given are kept
+    from the enclosing block, and each block restores the previous ones."""
+    unknown = set(kw) - set(_overrides)
+    if unknown:
+        raise TypeError(f"unknown plan overrides {sorted(unknown)}")
+    prev = dict(_overrides)
+    new = dict(prev)
+    new.update({k: int(v) for k, v in kw.items()})
+
+    def apply(o):
+        _check(load().i8g_set_test_overrides(o["force_tile"], o["force_splits"], o["qcols_two_pass"],
+                                             o["int4_direct"]))
+        _overrides.update(o)
+
+    apply(new)
+    try:
+        yield
+    finally:
+        apply(prev)
+
+
+def plan_query(M, N, K, ldc=None, flags=0):
+    """(tile configuration, K splits) that gemm_i8_blockscaled would use now."""
+    cfg, splits = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().i8g_plan_query(M, N, K, N if ldc is None else ldc, flags, ctypes.byref(cfg),
+                                 ctypes.byref(splits)))
+    return cfg.value, splits.value
 
 
 def hash_value(h) -> int:

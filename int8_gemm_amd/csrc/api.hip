@@ -312,6 +312,28 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
                       workspace_bytes, as_stream(stream), -2, 0);
 }
 
+int i8g_set_test_overrides(int32_t force_tile, int32_t force_splits, int32_t qcols_two_pass,
+                           int32_t int4_direct) {
+  if (force_tile < -1 || force_tile >= kNumGemmCfgs || force_splits < 0 || force_splits > 64)
+    return I8G_EINVAL;
+  set_test_overrides(force_tile, force_splits, qcols_two_pass ? 1 : 0, int4_direct ? 1 : 0);
+  return I8G_OK;
+}
+
+int i8g_plan_query(int64_t M, int64_t N, int64_t K, int64_t ldc, uint32_t flags, int32_t* config,
+                   int32_t* splits) {
+  if (M < 1 || N < 1 || K < 0 || M > INT32_MAX || N > INT32_MAX || ldc < N || !config || !splits)
+    return I8G_EINVAL;
+  if (flags & ~(I8G_RELU | I8G_HASH | I8G_A_INT4 | I8G_B_INT4)) return I8G_EINVAL;
+  const bool int4 = (flags & (I8G_A_INT4 | I8G_B_INT4)) != 0;
+  const GemmPlan plan = (int4 && int4_direct_requested())
+                            ? plan_gemm_int4(M, N, K > 0 ? K : 1, -1)
+                            : plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc);
+  *config = plan.cfg;
+  *splits = plan.splits;
+  return I8G_OK;
+}
+
 int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* hash, void* workspace,
                 size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || !hash) return I8G_EINVAL;

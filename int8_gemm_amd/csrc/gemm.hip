@@ -28,8 +28,8 @@
 //    computes the tile's share of the output hash S = sum c(j)*r(i)*bits(i,j)
 //    mod 2^64; the workgroup that finishes last adds the shares (mod 2^64,
 //    any order) and writes H (see hash_share_and_finalize).
+#include <atomic>
 #include <cmath>
-#include <cstdlib>
 #include <type_traits>
 
 #include "i8g_device.h"
@@ -1878,7 +1878,8 @@ static const TileCfg kCfgs[] = {
     {128, 192, 1, 3.7e12, 0, 5.5e-6, true, 128},  // persistent, 128-byte stages, 64x96 per wave
     {128, 128, 2, 1.75e12, 0, 4.5e-6, true, 128}, // the same, 64x64 per wave, two workgroups per CU
 };
-constexpr int kNumCfgs = 8;
+constexpr int kNumCfgs = kNumGemmCfgs;
+static_assert(sizeof(kCfgs) / sizeof(kCfgs[0]) == kNumCfgs, "one entry per configuration");
 constexpr int kPersistStages = 4;
 
 // Compute units of the current device (cached per device).
@@ -1895,26 +1896,33 @@ static int device_cus() {
   return cache[dev];
 }
 
-// Optional overrides for tests (the output never depends on the plan):
-// I8G_FORCE_TILE = index into kCfgs; I8G_FORCE_SPLITS = number of K splits
-// (clamped so that no split is empty).
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
+// Plan overrides set by i8g_set_test_overrides (tests only; the output
+// never depends on the plan).  Read once per plan, never from the
+// environment.
+static std::atomic<int> g_force_tile{-1}, g_force_splits{0}, g_qcols_two_pass{0}, g_int4_direct{0};
+
+void set_test_overrides(int force_tile, int force_splits, int qcols_two_pass, int int4_direct) {
+  g_force_tile.store(force_tile, std::memory_order_relaxed);
+  g_force_splits.store(force_splits, std::memory_order_relaxed);
+  g_qcols_two_pass.store(qcols_two_pass, std::memory_order_relaxed);
+  g_int4_direct.store(int4_direct, std::memory_order_relaxed);
 }
+
+bool qcols_two_pass_requested() { return g_qcols_two_pass.load(std::memory_order_relaxed) != 0; }
 
 constexpr int kCfgInt4 = kNumCfgs;   // gemm_i4_kernel, planned as the 128x128 tile
 
 GemmPlan plan_gemm_int4(int64_t M, int64_t N, int64_t K, int force_splits) {
   GemmPlan plan = plan_gemm_forced(M, N, K, false, 2,
-                                   force_splits < 0 ? env_int("I8G_FORCE_SPLITS", 0) : force_splits);
+                                   force_splits < 0 ? g_force_splits.load(std::memory_order_relaxed)
+                                                    : force_splits);
   if (plan.bm != 0) plan.cfg = kCfgInt4;
   return plan;
 }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent) {
-  return plan_gemm_forced(M, N, K, allow_persistent, env_int("I8G_FORCE_TILE", -1),
-                          env_int("I8G_FORCE_SPLITS", 0));
+  return plan_gemm_forced(M, N, K, allow_persistent, g_force_tile.load(std::memory_order_relaxed),
+                          g_force_splits.load(std::memory_order_relaxed));
 }
 
 GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent, int force_tile,
@@ -1948,7 +1956,7 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
       // rounds of tiles (MLP up-projection 8192x3072x768: 35 against 38 us);
       // slower on the LM head's 50 rounds at K = 768 (706 against ~680 us
       // for tile 0) and its K = 8192 weight gradient (375 against ~355 us)
-      if (t.per_cu > 1 && (K > 1024 || tiles > 8 * grid)) continue;
+      if (t.per_cu > 1 && force_tile < 0 && (K > 1024 || tiles > 8 * grid)) continue;
       const double rounds = std::ceil((double)tiles / (double)grid);
       double cost = rounds * ((double)t.bm * t.bn * K / t.wg_macs + t.tile_overhead);
       const double wr = (double)M * N * 4 / write_bw;
@@ -1967,7 +1975,7 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
       }
       continue;
     }
-    const double slots = 256.0 * t.per_cu;
+    const double slots = (double)cus * t.per_cu;
     for (int s = 1; s <= 16; ++s) {
       if (force_splits > 0) {
         if (s != (force_splits < kstages ? force_splits : (int)kstages)) continue;
@@ -2084,7 +2092,7 @@ __global__ void fill_zero_u32_kernel(unsigned int* p, int n) {
 }
 
 GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K) {
-  int force = env_int("I8G_FORCE_TILE", -1);
+  int force = g_force_tile.load(std::memory_order_relaxed);
   if (force > 2) force = -1;
   return plan_gemm_forced(M, N, K, false, force, 1);
 }
@@ -2158,9 +2166,6 @@ hipError_t launch_widen_int4(const int8_t* P, int64_t ldp, int64_t rows, int64_t
   return hipGetLastError();
 }
 
-bool int4_direct_requested() {
-  const char* v = getenv("I8G_INT4_DIRECT");
-  return v && v[0] == '1';
-}
+bool int4_direct_requested() { return g_int4_direct.load(std::memory_order_relaxed) != 0; }
 
 }  // namespace i8g

@@ -53,11 +53,15 @@ struct GemmPlan {
 // offsets; larger leading dimensions are planned without it.
 constexpr int64_t kPersistMaxLdc = int64_t(1) << 23;
 
+// Number of tile configurations of the planner (indices 0 .. kNumGemmCfgs-1;
+// kNumGemmCfgs itself denotes the direct int4 kernel).
+constexpr int kNumGemmCfgs = 8;
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_persistent);
 // The same with the tile configuration and split count forced (-1 / 0: the
 // cost model's choice); a configuration that cannot run the shape falls back
-// to the 128x128 tile.  plan_gemm reads them from I8G_FORCE_TILE /
-// I8G_FORCE_SPLITS (tests only).
+// to the 128x128 tile (i8g_plan_query shows which plan a shape gets).
+// plan_gemm takes them from the test overrides (set_test_overrides).
 GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent, int force_tile,
                           int force_splits);
 // Validates, plans and enqueues one GEMM exactly as gemm_i8_blockscaled does
@@ -68,19 +72,24 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
                  uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,
                  hipStream_t stream, int force_tile, int force_splits);
 // Plan for int4 operands: the register-staged kernel, 128x128 tiles, split
-// K as the cost model of that tile chooses (force_splits as above; < 0 reads
-// I8G_FORCE_SPLITS).
+// K as the cost model of that tile chooses (force_splits as above; < 0 takes
+// the test override).
 GemmPlan plan_gemm_int4(int64_t M, int64_t N, int64_t K, int force_splits);
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream);
 // int4 operands are by default widened to int8 codes in the workspace (rows
 // of int4_widened_ld(K) bytes) and multiplied by the int8 kernels;
-// I8G_INT4_DIRECT=1 (tests) selects gemm_i4_kernel, which reads the packed
-// bytes itself.
+// the int4_direct test override selects gemm_i4_kernel, which reads the
+// packed bytes itself.
 int64_t int4_widened_ld(int64_t K);
 hipError_t launch_widen_int4(const int8_t* P, int64_t ldp, int64_t rows, int64_t K, int8_t* Q,
                              hipStream_t stream);
 bool int4_direct_requested();
-// Requantizing epilogue: one K split, a non-persistent tile (I8G_FORCE_TILE
+// Test overrides (i8g_set_test_overrides): forced tile configuration (-1:
+// none) and split count (0: none), column quantize through the two-pass
+// kernels, int4 operands through gemm_i4_kernel.  Process-wide.
+void set_test_overrides(int force_tile, int force_splits, int qcols_two_pass, int int4_direct);
+bool qcols_two_pass_requested();
+// Requantizing epilogue: one K split, a non-persistent tile (a forced tile
 // 0..2 honoured for tests); the workspace adds M words of row maxima.
 GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K);
 size_t requant_rowmax_offset(const GemmPlan& plan);

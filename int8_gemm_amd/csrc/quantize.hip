@@ -17,8 +17,6 @@
 //  * cols, tall columns (bands of at most 8 columns would not read whole
 //    cache lines): two passes over X, a column-scale pass and a
 //    quantize-transpose pass (see qcols_scale_kernel).
-#include <cstdlib>
-
 #include "i8g_device.h"
 #include "i8g_launch.h"
 
@@ -489,10 +487,9 @@ hipError_t quantize_cols_int8(const float* X, int64_t rows, int64_t cols, int64_
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Qt % 16 == 0) && (ldqt % 16 == 0);
   int bc = rows > 0 ? qcols_band(rows, cols) : 0;
-  // I8G_QCOLS_TWO_PASS=1 forces the two-pass kernels (tests and timing; the
-  // bytes never depend on the path)
-  const char* force = getenv("I8G_QCOLS_TWO_PASS");
-  if (force && force[0] == '1') bc = 0;
+  // the test override forces the two-pass kernels (the bytes never depend
+  // on the path)
+  if (qcols_two_pass_requested()) bc = 0;
   if (bc > 0) {
     const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
     switch (bc) {
@@ -610,8 +607,7 @@ hipError_t quantize_cols_int4(const float* X, int64_t rows, int64_t cols, int64_
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   // up to 8192 rows: the one-kernel band path, packing as it stores
   int bc = rows > 0 ? qcols_band(rows, cols) : 0;
-  const char* force = getenv("I8G_QCOLS_TWO_PASS");
-  if (force && force[0] == '1') bc = 0;
+  if (qcols_two_pass_requested()) bc = 0;
   if (bc > 0) {
     const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
     switch (bc) {
@@ -735,8 +731,7 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
   }
   q.vec_out = ((uintptr_t)Q % 16 == 0) && (ldq % 16 == 0);
   const int bc = qcols_band(rows, cols);
-  const char* force = getenv("I8G_QCOLS_TWO_PASS");
-  if (bc == 0 || (force && force[0] == '1')) return false;   // the multi-kernel path
+  if (bc == 0 || qcols_two_pass_requested()) return false;   // the multi-kernel path
   q.kind = QK_COLS_REG; q.param = bc;
   q.blocks = (int)((cols + bc - 1) / bc);
   return true;

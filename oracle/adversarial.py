@@ -2,11 +2,13 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-The DaisyChain-Train page "Verification — why you can trust the numbers"
-(section "Layer 1: exact init gates", its last paragraph) gates the gate:
-it looks for an input on which an old and a new quantize spec disagree and
-requires the GPU to match the new one, so that a pass cannot be vacuous.
-These helpers build such inputs for the readings this oracle takes:
+A bit-exact comparison proves nothing about a rounding rule unless some
+input actually exercises it: on ordinary data, several competing readings of
+the quantizer produce identical bytes.  These helpers construct inputs on
+which those readings give different int8 values, so that a GPU matching the
+oracle there has followed the reading this oracle takes (the DaisyChain-Train
+page "Verification — why you can trust the numbers", section "Layer 1: exact
+init gates", asks for such discriminating inputs):
 
 * :func:`plant_ties` -- entries x with RN(x * inv) = k + 0.5 exactly, for
   scales that are not powers of two (half-up rounding vs ties-to-even vs

@@ -87,3 +87,29 @@ def test_argument_checks_of_the_extended_entry_points():
     assert lib.gemm_i8_requant_workspace_bytes(M, N, K) >= 256 + 4 * M
     assert lib.gemm_i8_requant_workspace_bytes(0, N, K) == 256
     assert lib.i8g_status_string(6).startswith(b"self-check failed")
+
+
+def test_test_overrides_and_plan_query():
+    """The test hooks are explicit calls (no environment variable is read on
+    the plan path): the override entry point validates its arguments and the
+    plan query reports what the planner picks under it (host-only logic)."""
+    import int8_gemm_amd as g
+    lib = g.load()
+    assert lib.i8g_set_test_overrides(8, 0, 0, 0) == 1        # no tile configuration 8
+    assert lib.i8g_set_test_overrides(-2, 0, 0, 0) == 1
+    assert lib.i8g_set_test_overrides(-1, -1, 0, 0) == 1
+    with pytest.raises(g.I8GError):
+        g.plan_query(0, 5, 5)
+    free_cfg, free_splits = g.plan_query(1000, 1000, 1024)
+    with g.plan_overrides(force_tile=2, force_splits=4):
+        assert g.plan_query(1000, 1000, 1024) == (2, 4)
+        with g.plan_overrides(force_splits=0):                 # nested: the tile stays forced
+            assert g.plan_query(1000, 1000, 1024) == (2, 1)
+        assert g.plan_query(1000, 1000, 1024) == (2, 4)
+    assert g.plan_query(1000, 1000, 1024) == (free_cfg, free_splits)
+    # a forced two-workgroups-per-CU tile runs beyond the K the cost model
+    # keeps it to (it is still correct there, only slower)
+    with g.plan_overrides(force_tile=7):
+        assert g.plan_query(2048, 2000, 1536) == (7, 1)
+    with g.plan_overrides(int4_direct=True):
+        assert g.plan_query(96, 200, 4160, flags=g.I8G_B_INT4)[0] == 8

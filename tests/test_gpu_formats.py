@@ -2,7 +2,6 @@
 int8 / int4 values, absmax / power-of-two scales) against oracle/formats.py,
 bit for bit: quantize outputs (int4: the packed bytes), GEMM outputs and
 hashes with int4 operands."""
-import os
 
 import numpy as np
 import pytest
@@ -85,13 +84,11 @@ GSHAPES = [(1, 1, 1), (17, 33, 15), (130, 190, 70), (300, 520, 192), (256, 256, 
 
 
 @pytest.fixture(params=["widened", "direct"])
-def int4_path(request):
+def int4_path(request, g):
     """int4 operands widened to int8 for the int8 kernels (the default), or
-    read packed by gemm_i4_kernel (I8G_INT4_DIRECT=1)."""
-    if request.param == "direct":
-        os.environ["I8G_INT4_DIRECT"] = "1"
-    yield request.param
-    os.environ.pop("I8G_INT4_DIRECT", None)
+    read packed by gemm_i4_kernel (the int4_direct plan override)."""
+    with g.plan_overrides(int4_direct=request.param == "direct"):
+        yield request.param
 
 
 @pytest.mark.parametrize("combo", [(True, False), (False, True), (True, True)])
@@ -125,8 +122,8 @@ def test_gemm_int4_forced_splits(g, int4_path):
     A = rng.standard_normal((M, K)).astype(np.float32)
     B = rng.standard_normal((K, N)).astype(np.float32)
     C_ref, QA, sr, QB, sc = F.blockscaled_gemm(A, B, F.INT4, F.INT4)
-    os.environ["I8G_FORCE_SPLITS"] = "5"
-    try:
+    with g.plan_overrides(force_splits=5):
+        assert g.plan_query(M, N, K, flags=g.I8G_B_INT4)[1] == 5
         for a4 in (True, False):
             say("gemm int4 split", a4)
             QA_use = QA if a4 else ref.quantize_rows(A)[0]
@@ -137,8 +134,6 @@ def test_gemm_int4_forced_splits(g, int4_path):
                                       torch.from_numpy(sc).cuda(), K=K, a_int4=a4, b_int4=True)
             torch.cuda.synchronize()
             assert np.array_equal(C.cpu().numpy().view(np.uint32), want.view(np.uint32))
-    finally:
-        del os.environ["I8G_FORCE_SPLITS"]
 
 
 def test_whole_method_int4_weights_mlp_down(g, int4_path):
@@ -174,12 +169,10 @@ def test_int4_weights_on_persistent_tiles(g, tile):
     dA, dsr = g.quantize_rows(torch.from_numpy(A).cuda())
     dB, dsc = g.quantize_cols_fmt(torch.from_numpy(B).cuda(), F.INT4)
     say("int4 weights tile", tile)
-    os.environ["I8G_FORCE_TILE"] = str(tile)
-    try:
+    with g.plan_overrides(force_tile=tile):
+        assert g.plan_query(M, N, K, flags=g.I8G_B_INT4)[0] == tile, "the forced plan did not run"
         C, h = g.gemm_i8_blockscaled(dA, dsr, dB, dsc, relu=True, want_hash=True, K=K, b_int4=True)
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("I8G_FORCE_TILE", None)
     assert np.array_equal(C.cpu().numpy().view(np.uint32), C_ref.view(np.uint32))
     assert g.hash_value(h) == hashref.output_hash(C_ref)
 
@@ -207,13 +200,9 @@ def test_int4_columns_both_paths(g, fmt, two_pass, shape):
     rows, cols = shape
     say("int4 cols", fmt, "two_pass", two_pass, rows, cols)
     X = _data(rows + cols + fmt, rows, cols)
-    if two_pass:
-        os.environ["I8G_QCOLS_TWO_PASS"] = "1"
-    try:
+    with g.plan_overrides(qcols_two_pass=two_pass):
         Qt, st = g.quantize_cols_fmt(torch.from_numpy(X).cuda(), fmt)
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("I8G_QCOLS_TWO_PASS", None)
     qc, sc = F.quantize_cols(X, fmt)
     assert np.array_equal(st.cpu().numpy().view(np.uint32), sc.view(np.uint32))
     assert np.array_equal(_bytes(Qt), F.pack_int4(qc))

@@ -7,7 +7,6 @@ in its init gates ("Layer 1: exact init gates") for exactly this reason.
 
 Every case prints its name before it touches the GPU.
 """
-import os
 
 import numpy as np
 import pytest
@@ -15,6 +14,7 @@ import torch
 
 from oracle import adversarial, hashref, ref
 from synth import inputs as S
+from tests.parity import assert_bits, check_against_oracle
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -45,31 +45,6 @@ def run_method(g, A, B, relu, want_hash=True):
     torch.cuda.synchronize()
     return dict(QA=QA.cpu().numpy(), s_row=sr.cpu().numpy(), QBt=QBt.cpu().numpy(),
                 s_col=sc.cpu().numpy(), C=C.cpu().numpy(), hash=g.hash_value(h))
-
-
-def assert_bits(got, want, what):
-    got = np.asarray(got)
-    want = np.asarray(want)
-    assert got.shape == want.shape, (what, got.shape, want.shape)
-    if got.dtype == np.float32:
-        bad = got.view(U32) != want.view(U32)
-    else:
-        bad = got != want
-    if bad.any():
-        idx = np.argwhere(bad)[:5]
-        detail = [(tuple(i), got[tuple(i)], want[tuple(i)]) for i in idx]
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} differ, e.g. {detail}")
-
-
-def check_against_oracle(got, A, B, relu):
-    C, QA, s_row, QBt, s_col = ref.blockscaled_gemm(A, B, relu)
-    assert_bits(got["QA"], QA, "QA")
-    assert_bits(got["s_row"], s_row, "s_row")
-    assert_bits(got["QBt"], QBt, "QBt")
-    assert_bits(got["s_col"], s_col, "s_col")
-    assert_bits(got["C"], C, "C")
-    assert got["hash"] == hashref.output_hash(C), "hash"
-    return C
 
 
 def adversarial_inputs(c):
@@ -140,12 +115,9 @@ def test_quantize_cols_two_pass(g, rows, cols):
     scales, then quantize-transpose) on every shape, forced."""
     say("quantize_cols two-pass", rows, cols)
     X = np.ascontiguousarray(_quant_input(cols, rows, rows * 7919 + cols + 1).T)
-    os.environ["I8G_QCOLS_TWO_PASS"] = "1"
-    try:
+    with g.plan_overrides(qcols_two_pass=True):
         Qt, s = g.quantize_cols(to_dev(X))
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("I8G_QCOLS_TWO_PASS", None)
     Qo, so = ref.quantize_cols(X)
     assert_bits(Qt.cpu().numpy(), Qo, "Qt")
     assert_bits(s.cpu().numpy(), so, "scale")
@@ -191,17 +163,13 @@ def test_tile_and_split_invariance(g, tile):
     B = rng.standard_normal((3000, 520)).astype(F32)
     C, *_ = ref.blockscaled_gemm(A, B, True)
     h = hashref.output_hash(C)
-    try:
-        for splits in (1, 2, 5, 16):
-            os.environ["I8G_FORCE_TILE"] = str(tile)
-            os.environ["I8G_FORCE_SPLITS"] = str(splits)
+    for splits in (1, 2, 5, 16):
+        with g.plan_overrides(force_tile=tile, force_splits=splits):
+            assert g.plan_query(300, 520, 3000) == (tile, splits), "the forced plan did not run"
             say("invariance tile", tile, "splits", splits)
             got = run_method(g, A, B, relu=True)
-            assert_bits(got["C"], C, f"C tile {tile} splits {splits}")
-            assert got["hash"] == h
-    finally:
-        os.environ.pop("I8G_FORCE_TILE", None)
-        os.environ.pop("I8G_FORCE_SPLITS", None)
+        assert_bits(got["C"], C, f"C tile {tile} splits {splits}")
+        assert got["hash"] == h
 
 
 # (M, N, K, relu): ragged edges; more tiles than CUs so that workgroups walk
@@ -216,17 +184,15 @@ def test_persistent_kernel(g, tile):
     """The persistent kernel (epilogue of one tile drained under the next
     tile's MFMAs) against the oracle, every byte and the hash."""
     rng = np.random.default_rng(90 + tile)
-    try:
-        os.environ["I8G_FORCE_TILE"] = str(tile)
+    with g.plan_overrides(force_tile=tile):
         for (m, n, k, relu) in PERSIST_CASES:
             A = rng.standard_t(3, (m, k)).astype(F32)
             B = rng.standard_normal((k, n)).astype(F32)
             A[rng.random(m) < 0.02] = 0
             say("persistent tile", tile, "MNK", m, n, k, "relu", relu)
+            assert g.plan_query(m, n, k) == (tile, 1), "the forced plan did not run"
             got = run_method(g, A, B, relu=relu)
             check_against_oracle(got, A, B, relu)
-    finally:
-        os.environ.pop("I8G_FORCE_TILE", None)
 
 
 # 128-byte-stage persistent kernel: M % 128 == 0, K % 128 == 0, K / 128 at
@@ -246,18 +212,18 @@ def test_persistent128_kernel(g, tile):
     """The persistent kernels with 128-byte K stages against the oracle, every
     byte and the hash."""
     rng = np.random.default_rng(96 + tile)
-    try:
-        os.environ["I8G_FORCE_TILE"] = str(tile)
+    with g.plan_overrides(force_tile=tile):
         for (m, n, k, relu) in PERSIST128_CASES:
+            if tile == 6 and k < 768:
+                continue                  # below tile 6's bound: another tile would run
             A = rng.standard_t(3, (m, k)).astype(F32)
             B = rng.standard_normal((k, n)).astype(F32)
             A[rng.random(m) < 0.02] = 0
             B[:, rng.random(n) < 0.02] = 0
             say("persistent128 tile", tile, "MNK", m, n, k, "relu", relu)
+            assert g.plan_query(m, n, k) == (tile, 1), "the forced plan did not run"
             got = run_method(g, A, B, relu=relu)
             check_against_oracle(got, A, B, relu)
-    finally:
-        os.environ.pop("I8G_FORCE_TILE", None)
 
 
 def test_w2_mlp_full_size(g):
@@ -307,14 +273,12 @@ def test_max_k_int32_limit(g, splits):
     dA[:, :K] = torch.from_numpy(QA).cuda()
     dB[:, :K] = torch.from_numpy(QB).cuda()
     say("max K", M, N, K, "splits", splits)
-    if splits:
-        os.environ["I8G_FORCE_SPLITS"] = str(splits)
-    try:
+    with g.plan_overrides(force_splits=splits):
+        if splits:
+            assert g.plan_query(M, N, K)[1] == splits
         C, h = g.gemm_i8_blockscaled(dA[:, :K], torch.from_numpy(sr).cuda(), dB[:, :K],
                                      torch.from_numpy(sc).cuda(), want_hash=True)
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("I8G_FORCE_SPLITS", None)
     assert np.array_equal(C.cpu().numpy().view(np.uint32), want.view(np.uint32))
     assert g.hash_value(h) == hashref.output_hash(want)
 
@@ -337,13 +301,11 @@ def test_output_leading_dimension(g, case):
     dQA, dsA = g.quantize_rows(torch.from_numpy(A).cuda())
     dQB, dsB = g.quantize_cols(torch.from_numpy(B).cuda())
     buf = torch.full((M, ldc), -7.25, dtype=torch.float32, device="cuda")
-    if tile is not None:
-        os.environ["I8G_FORCE_TILE"] = str(tile)
-    try:
+    with g.plan_overrides(force_tile=-1 if tile is None else tile):
+        if tile is not None:
+            assert g.plan_query(M, N, K, ldc=ldc)[0] == tile, "the forced plan did not run"
         C, h = g.gemm_i8_blockscaled(dQA, dsA, dQB, dsB, relu=True, want_hash=True, out=buf[:, :N])
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("I8G_FORCE_TILE", None)
     got = buf[:, :N].cpu().numpy()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     pad = buf[:, N:min(ldc, N + 4096)]
@@ -417,11 +379,9 @@ def test_workspace_scratch_contents_do_not_matter(g):
     for it in range(3):
         for ws in g._ws.values():
             ws[256:].random_(0, 256)
-        os.environ["I8G_FORCE_SPLITS"] = "3"
-        try:
+        with g.plan_overrides(force_splits=3):
+            assert g.plan_query(700, 300, 9000)[1] == 3
             got = run_method(g, A, B, relu=False)
-        finally:
-            os.environ.pop("I8G_FORCE_SPLITS", None)
         assert_bits(got["C"], C, f"C call {it}")
         assert got["hash"] == hashref.output_hash(C)
         for ws in g._ws.values():

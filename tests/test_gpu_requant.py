@@ -2,7 +2,6 @@
 oracle (oracle/requant.py: quantize_rows of the method's output) and against
 the library's own two-call path, bit for bit, with the hash of the f32 output
 that the call never stores."""
-import os
 
 import numpy as np
 import pytest
@@ -61,12 +60,9 @@ def test_requant_every_tile(g, tile):
     say("requant tile", tile)
     (QA, sA, QB, sB), dev = _operands(g, M, N, K, 77)
     Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, True)
-    os.environ["I8G_FORCE_TILE"] = str(tile)
-    try:
+    with g.plan_overrides(force_tile=tile):
         Q, s, h = g.gemm_i8_requant(*dev, relu=True, want_hash=True)
         torch.cuda.synchronize()
-    finally:
-        del os.environ["I8G_FORCE_TILE"]
     assert np.array_equal(Q.cpu().numpy(), Qw) and np.array_equal(s.cpu().numpy(), sw)
     assert g.hash_value(h) == hashref.output_hash(Cw)
 
