@@ -40,8 +40,10 @@
  *     unspecified bytes.
  *   - Empty shapes (a zero dimension) are valid and enqueue nothing except
  *     the hash of an empty output where one is requested.
- *   - The library allocates no device memory.  Calls that share a
- *     workspace must be ordered (same stream, or synchronized).
+ *   - The library allocates no device memory at run time.  Calls that
+ *     share a workspace must be ordered (same stream, or synchronized).
+ *     gemm_i8_blockscaled_noalloc uses a static device buffer instead of a
+ *     workspace (see there).
  *   - No kernel waits on another workgroup and no call synchronizes with
  *     the host: grid-wide sums end in the workgroup that finishes last.
  */
@@ -65,6 +67,8 @@ extern "C" {
 #define I8G_EHIP        5  /* the HIP runtime reported a launch error        */
 #define I8G_EGATE       6  /* i8g_gate: a device output differs from the     */
                            /* exact host mirror (see i8g_gate_report)        */
+#define I8G_ESCRATCH    7  /* gemm_i8_blockscaled_noalloc: the shape needs   */
+                           /* more scratch than its static buffer holds      */
 
 /* flags of gemm_i8_blockscaled */
 #define I8G_RELU 1u        /* fused ReLU: out = out > 0 ? out : +0          */
@@ -202,6 +206,34 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row,
                         int64_t M, int64_t N, int64_t K,
                         float* C, int64_t ldc, uint32_t flags, uint64_t* hash,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gemm_i8_blockscaled_noalloc -- gemm_i8_blockscaled without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *   Arguments, outputs, layouts and rules as gemm_i8_blockscaled.
+ *   Scratch: the call's workspace is a static device array of the library
+ *   (I8G_NOALLOC_SCRATCH_BYTES = 64 MiB, one per GPU the library runs on,
+ *   held until the process ends).  Its address is looked up, and its
+ *   control header zeroed by a small kernel on `stream`, at the first call
+ *   on each device; every call leaves the header zero again.  Nothing is
+ *   allocated by any call (no hipMalloc, no allocating library routine).
+ *   A shape whose plan needs more scratch than the array holds (gemm_i8_
+ *   workspace_bytes_flags of the plan taken: int32 partial sums of a split
+ *   K, int4 operands widened to int8) returns I8G_ESCRATCH before anything
+ *   is enqueued; without a split K every GPT-2-small shape fits.
+ *   Calls on one GPU share its array: calls that overlap in time on one GPU
+ *   (different streams not ordered by the caller, or different threads)
+ *   race and give unspecified bytes; calls ordered on one stream are safe.
+ * Errors: as gemm_i8_blockscaled, plus I8G_ESCRATCH; I8G_EHIP also when the
+ * array's device address cannot be obtained.
+ */
+#define I8G_NOALLOC_SCRATCH_BYTES 67108864u   /* 64 MiB */
+int gemm_i8_blockscaled_noalloc(const int8_t* QA, int64_t lda, const float* s_row,
+                                const int8_t* QBt, int64_t ldb, const float* s_col,
+                                int64_t M, int64_t N, int64_t K,
+                                float* C, int64_t ldc, uint32_t flags, uint64_t* hash,
+                                void* stream);
 
 /* Bytes of workspace gemm_i8_blockscaled needs for this shape (>= 256),
  * for int8 operands. */

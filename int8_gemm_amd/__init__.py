@@ -44,7 +44,7 @@ EXPORTED = ("quantize_rows", "quantize_cols", "gemm_i8_blockscaled", "gemm_i8_wo
             "i8g_probe_hash", "i8g_probe_workspace_bytes", "quantize_rows_fmt", "quantize_cols_fmt",
             "gemm_i8_requant", "gemm_i8_requant_workspace_bytes", "quantize_batch",
             "gemm_i8_workspace_bytes_flags", "i8g_audit_quantize_fmt", "i8g_set_test_overrides",
-            "i8g_plan_query")
+            "i8g_plan_query", "gemm_i8_blockscaled_noalloc")
 
 _lib = None
 _ws = {}
@@ -118,6 +118,9 @@ def load():
     lib.i8g_probe_hash.argtypes = [ctypes.c_uint64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
     lib.i8g_probe_hash.restype = ctypes.c_int
     c_i32 = ctypes.c_int32
+    lib.gemm_i8_blockscaled_noalloc.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64,
+                                                c_i64, c_vp, c_i64, c_u32, c_vp, c_vp]
+    lib.gemm_i8_blockscaled_noalloc.restype = ctypes.c_int
     lib.i8g_set_test_overrides.argtypes = [c_i32, c_i32, c_i32, c_i32]
     lib.i8g_set_test_overrides.restype = ctypes.c_int
     lib.i8g_plan_query.argtypes = [c_i64, c_i64, c_i64, c_i64, c_u32, ctypes.POINTER(c_i32),
@@ -306,6 +309,31 @@ def gemm_i8_blockscaled(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=
         _ptr(QA), lda, _ptr(s_row), _ptr(QBt), ldb, _ptr(s_col), M, N, K,
         _ptr(C), max(C.stride(0), N, 1), flags, _ptr(h), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(QA)))
+    return (C, h) if want_hash else C
+
+
+def gemm_i8_blockscaled_noalloc(QA, s_row, QBt, s_col, relu=False, want_hash=False, out=None):
+    """gemm_i8_blockscaled through the entry point that allocates nothing (its
+    scratch is the library's static device array): int8 operands only.  The
+    output (and hash tensor) are allocated here unless `out` is given."""
+    _req_matrix(QA, torch.int8, "QA")
+    _req_matrix(QBt, torch.int8, "QBt")
+    M, K = QA.shape
+    N, K2 = QBt.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: QA has {K}, QBt has {K2}")
+    if s_row.numel() != M or s_col.numel() != N or s_row.dtype != torch.float32 or \
+            s_col.dtype != torch.float32 or not (s_row.is_contiguous() and s_col.is_contiguous()):
+        raise ValueError("scales must be contiguous float32 of lengths M and N")
+    dev = QA.device
+    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _req_matrix(C, torch.float32, "out")
+    h = torch.zeros(1, dtype=torch.int64, device=dev) if want_hash else None
+    flags = (I8G_RELU if relu else 0) | (I8G_HASH if want_hash else 0)
+    _check(load().gemm_i8_blockscaled_noalloc(
+        _ptr(QA), QA.stride(0) if M > 0 else _round16(K), _ptr(s_row), _ptr(QBt),
+        QBt.stride(0) if N > 0 else _round16(K), _ptr(s_col), M, N, K, _ptr(C), max(C.stride(0), N, 1),
+        flags, _ptr(h), _stream(QA)))
     return (C, h) if want_hash else C
 
 

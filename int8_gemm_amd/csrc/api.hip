@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/int8_gemm.h"
@@ -18,6 +19,43 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? I8G_OK : I8G_EHIP; }
 
+// ---------------------------------------------------------------------------
+// Scratch of gemm_i8_blockscaled_noalloc: a file-scope device array (one copy
+// per GPU, from the code object's load until the process ends).  In host
+// code its name is only a stand-in for the device symbol: the device address
+// comes from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoallocScratchBytes = I8G_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Zeroes the workspace control header (64 words); a kernel rather than a
+// memset, so that a caller capturing the stream into a HIP graph records a
+// kernel node.
+__global__ void zero_header_kernel(unsigned int* h) { h[threadIdx.x] = 0u; }
+
+// The scratch array's device address on the current device; at the first
+// call on a device also enqueues the zeroing of its header on `stream`.
+int scratch_for_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return I8G_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return I8G_EHIP;
+    hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(kWsHeader / 4), 0, stream,
+                       reinterpret_cast<unsigned int*>(p));
+    if (hipGetLastError() != hipSuccess) return I8G_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return I8G_OK;
+}
+
 }  // namespace
 
 namespace i8g {
@@ -26,6 +64,10 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
                  const float* s_col, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
                  uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,
                  hipStream_t stream, int force_tile, int force_splits) {
+  // force_tile == -4: validate and plan only (the workspace pointer is not
+  // needed, its size is checked), enqueue nothing
+  const bool dry = force_tile == -4;
+  if (dry) force_tile = -2;
   if (M < 0 || N < 0 || K < 0) return I8G_EINVAL;
   if (M > INT32_MAX || N > INT32_MAX) return I8G_EINVAL;
   if (flags & ~(I8G_RELU | I8G_HASH | I8G_A_INT4 | I8G_B_INT4)) return I8G_EINVAL;
@@ -33,9 +75,10 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
   const bool want_hash = (flags & I8G_HASH) != 0;
   if (want_hash && !hash) return I8G_EINVAL;
   if (K > I8G_K_MAX) return I8G_EKRANGE;
-  if (!workspace || ((uintptr_t)workspace % 256) != 0) return I8G_EWORKSPACE;
+  if (!dry && (!workspace || ((uintptr_t)workspace % 256) != 0)) return I8G_EWORKSPACE;
   if (M == 0 || N == 0) {
     if (workspace_bytes < kWsHeader) return I8G_EWORKSPACE;
+    if (dry) return I8G_OK;
     if (want_hash) return hip_status(launch_output_hash(C, M, N, ldc, hash, workspace, stream));
     return I8G_OK;
   }
@@ -56,24 +99,25 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
                       ? plan_gemm(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc)
                       : plan_gemm_forced(M, N, K > 0 ? K : 1, ldc <= kPersistMaxLdc, force_tile, force_splits);
   if (workspace_bytes < plan.workspace_bytes) return I8G_EWORKSPACE;
+  const bool widen = (a4 || b4) && !direct4 && K > 0;   // int4 operands widened into the workspace
+  const int64_t ldw = widen ? int4_widened_ld(K) : 0;
+  const size_t wa_off = (plan.workspace_bytes + 255) / 256 * 256;
+  const size_t wa_bytes = (widen && a4) ? ((size_t)M * ldw + 255) / 256 * 256 : 0;
+  const size_t wb_bytes = (widen && b4) ? ((size_t)N * ldw + 255) / 256 * 256 : 0;
+  if (widen && workspace_bytes < wa_off + wa_bytes + wb_bytes) return I8G_EWORKSPACE;
+  if (dry) return I8G_OK;
   bool wa = false, wb = false;   // operands widened into the workspace
-  if ((a4 || b4) && !direct4 && K > 0) {
-    const int64_t ldw = int4_widened_ld(K);
-    size_t off = (plan.workspace_bytes + 255) / 256 * 256;
-    const size_t need = off + (a4 ? ((size_t)M * ldw + 255) / 256 * 256 : 0) +
-                        (b4 ? ((size_t)N * ldw + 255) / 256 * 256 : 0);
-    if (workspace_bytes < need) return I8G_EWORKSPACE;
+  if (widen) {
     char* ws = reinterpret_cast<char*>(workspace);
     if (a4) {
-      int8_t* w = reinterpret_cast<int8_t*>(ws + off);
+      int8_t* w = reinterpret_cast<int8_t*>(ws + wa_off);
       if (launch_widen_int4(QA, lda, M, K, w, stream) != hipSuccess) return I8G_EHIP;
       QA = w;
       lda = ldw;
-      off += ((size_t)M * ldw + 255) / 256 * 256;
       wa = true;
     }
     if (b4) {
-      int8_t* w = reinterpret_cast<int8_t*>(ws + off);
+      int8_t* w = reinterpret_cast<int8_t*>(ws + wa_off + wa_bytes);
       if (launch_widen_int4(QBt, ldb, N, K, w, stream) != hipSuccess) return I8G_EHIP;
       QBt = w;
       ldb = ldw;
@@ -124,6 +168,7 @@ const char* i8g_status_string(int status) {
     case I8G_EWORKSPACE: return "workspace missing, misaligned or smaller than gemm_i8_workspace_bytes()";
     case I8G_EHIP: return "HIP runtime error while enqueueing a kernel";
     case I8G_EGATE: return "self-check failed: a device output differs from the exact host mirror";
+    case I8G_ESCRATCH: return "the shape needs more scratch than the 64 MiB static buffer of gemm_i8_blockscaled_noalloc holds (a split K of a large output): use gemm_i8_blockscaled with a workspace";
     default: return "unknown status";
   }
 }
@@ -332,6 +377,24 @@ int i8g_plan_query(int64_t M, int64_t N, int64_t K, int64_t ldc, uint32_t flags,
   *config = plan.cfg;
   *splits = plan.splits;
   return I8G_OK;
+}
+
+int gemm_i8_blockscaled_noalloc(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,
+                                int64_t ldb, const float* s_col, int64_t M, int64_t N, int64_t K,
+                                float* C, int64_t ldc, uint32_t flags, uint64_t* hash, void* stream) {
+  const hipStream_t st = as_stream(stream);
+  // the same checks as gemm_i8_blockscaled, run on a stand-in workspace
+  // first, so that an invalid call or a shape whose plan needs more than the
+  // array holds returns before anything (even the header zeroing) is enqueued
+  const int pre = enqueue_gemm(QA, lda, s_row, QBt, ldb, s_col, M, N, K, C, ldc, flags, hash,
+                               nullptr, kNoallocScratchBytes, st, -4, 0);
+  if (pre == I8G_EWORKSPACE) return I8G_ESCRATCH;
+  if (pre != I8G_OK) return pre;
+  void* ws = nullptr;
+  const int s = scratch_for_device(st, &ws);
+  if (s != I8G_OK) return s;
+  return enqueue_gemm(QA, lda, s_row, QBt, ldb, s_col, M, N, K, C, ldc, flags, hash, ws,
+                      kNoallocScratchBytes, st, -2, 0);
 }
 
 int output_hash(const float* C, int64_t M, int64_t N, int64_t ldc, uint64_t* hash, void* workspace,

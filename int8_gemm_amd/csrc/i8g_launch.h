@@ -66,7 +66,9 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
                           int force_splits);
 // Validates, plans and enqueues one GEMM exactly as gemm_i8_blockscaled does
 // (force_tile / force_splits as in plan_gemm_forced; force_tile == -2 is the
-// library's own choice, -3 the direct int4 kernel for int4 operands).
+// library's own choice, -3 the direct int4 kernel for int4 operands, -4 the
+// library's choice validated and planned only: every status check, including
+// the workspace size, but nothing enqueued and the workspace pointer unused).
 int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt, int64_t ldb,
                  const float* s_col, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
                  uint32_t flags, uint64_t* hash, void* workspace, size_t workspace_bytes,

@@ -10,6 +10,7 @@ import pytest
 def _declared(repo_root):
     text = open(os.path.join(repo_root, "include", "int8_gemm.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^#.*$", "", text, flags=re.M)
     names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text)
     return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
 
@@ -36,7 +37,7 @@ def test_host_only_calls(repo_root):
     import int8_gemm_amd as g
     lib = g.load()
     assert lib.i8g_version().startswith(b"int8_gemm")
-    for st in range(7):
+    for st in range(8):
         assert lib.i8g_status_string(st)
     assert lib.i8g_status_string(99) == b"unknown status"
     assert g.workspace_bytes(256, 256, 256) >= 256
@@ -113,3 +114,24 @@ def test_test_overrides_and_plan_query():
         assert g.plan_query(2048, 2000, 1536) == (7, 1)
     with g.plan_overrides(int4_direct=True):
         assert g.plan_query(96, 200, 4160, flags=g.I8G_B_INT4)[0] == 8
+
+
+def test_noalloc_argument_checks():
+    """gemm_i8_blockscaled_noalloc validates and plans on the host before
+    anything is enqueued (no device is touched by these calls): argument
+    errors as gemm_i8_blockscaled, and a plan needing more than the static
+    64 MiB scratch is refused with I8G_ESCRATCH."""
+    import int8_gemm_amd as g
+    lib = g.load()
+    P = ctypes.c_void_p
+    fake = P(1 << 20)                      # 16-byte aligned, never dereferenced
+    f = lib.gemm_i8_blockscaled_noalloc
+    assert f(fake, 64, fake, fake, 64, fake, -1, 8, 64, fake, 8, 0, None, None) == 1      # negative M
+    assert f(fake, 64, fake, fake, 64, fake, 8, 8, 64, fake, 8, 2, None, None) == 1       # hash without pointer
+    assert f(fake, 64, fake, fake, 64, fake, 8, 8, 200000, fake, 8, 0, None, None) == 2   # K beyond int32
+    assert f(P((1 << 20) + 1), 64, fake, fake, 64, fake, 8, 8, 64, fake, 8, 0, None, None) == 3
+    assert f(fake, 64, fake, fake, 64, fake, 8, 8, 64, fake, 8, 1 << 7, None, None) == 1  # unknown flag
+    with g.plan_overrides(force_tile=2, force_splits=2):
+        # two int32 partial planes of 4096 x 4096: 128 MiB > 64 MiB
+        assert f(fake, 8192, fake, fake, 8192, fake, 4096, 4096, 8192, fake, 4096, 0, None, None) == 7
+    assert lib.i8g_status_string(7).startswith(b"the shape needs more scratch")

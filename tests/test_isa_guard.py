@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 from int8_gemm_amd import build as B  # noqa: E402
 
-SOURCES = ["quantize.hip", "gemm.hip", "hash.hip", "verify.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "hash.hip", "verify.hip", "api.hip"]
 # kernels that must be present in the scanned code (the scan is not vacuous)
 EXPECTED = ["qrows_wave_kernel", "qrows_block_kernel", "qcols_reg_kernel", "qcols_scale_kernel",
             "qcols_quant_kernel", "quantize_batch_kernel", "q4rows_kernel", "gemm_i8_dma_kernel",
