@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the bit-exact block-scaled int8 GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload mlp|head|step|w1]
+    python bench.py [--steps K] [--warmup W] [--workload mlp|head|step|layer|w1]
                     [--b-format int8|pow2|int4|int4-pow2] [--requant]
 
 One step is one pass of the whole path over one batch: per GEMM, the
@@ -90,6 +90,22 @@ def make_workload(name):
         desc = ("GPT-2-small training step: the 147 GEMMs of 12 layers x (QKV, attention "
                 "out, MLP up, MLP down) forward, dgrad and wgrad plus the LM head "
                 "(8192 token rows); quantize passes included")
+        return desc, tensors, gemms
+    if name == "layer":
+        tensors, gemms = {}, []
+        for gm in S.step_gemms():
+            if not gm.linear.startswith("L0."):
+                continue
+            a, am, b, bm = gm.operands
+            for src in (a, b):
+                key = f"{gm.linear}.{src}"
+                if key not in tensors:
+                    tensors[key] = S.step_tensor(gm.linear, src, gm.d_in, gm.d_out)
+            gemms.append((f"{gm.linear}.{gm.kind}", f"{gm.linear}.{a}", am, f"{gm.linear}.{b}", bm,
+                          False, None))
+        desc = ("GPT-2-small layer: the 12 GEMMs of layer 0 of the training step (QKV, attention "
+                "out, MLP fc, MLP proj; forward, dgrad and wgrad each; 8192 token rows); quantize "
+                "passes included")
         return desc, tensors, gemms
     if name == "w1":
         A, B = S.w1_inputs()
@@ -592,7 +608,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "step", "w1"])
+    ap.add_argument("--workload", default="mlp", choices=["mlp", "head", "step", "layer", "w1"])
     ap.add_argument("--b-format", default="int8", choices=list(B_FORMATS),
                     help="storage format of every B operand (int4: two values per byte; "
                          "pow2: power-of-two scales); A operands stay int8 with absmax scales")

@@ -111,6 +111,15 @@ int quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx,
  *          It is also used as scratch while the call runs.
  * Qt[j,k] = floor(RN(RN(X[k,j] * RN(1/scale[j])) + 0.5)).
  * With rows == 0 only the scales are written (each is RN(1e-8)).
+ * Large inputs (at least 256 MiB of X, rows a multiple of 256 and at least
+ * 1024, cols a multiple of 32, X and Qt 16-byte aligned, ldx a multiple of 4
+ * and ldqt of 16) are quantized by a cooperative launch that reads X once:
+ * the workgroups sharing a band of columns exchange partial maxima through
+ * `scale` and a counter kept in the first four bytes of the band's first Qt
+ * row (written with the codes last), waiting for each other with a bounded
+ * wait.  The runtime keeps a cooperative grid resident (or the launch fails
+ * and the call takes the other path), so the wait ends; if it ever timed
+ * out, the band's scales are left NaN, which no valid call produces.
  * Errors: as quantize_rows (with the roles of rows and cols exchanged).
  */
 int quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
@@ -423,12 +432,14 @@ int i8g_probe_hash(uint64_t seed, int64_t M, int64_t N, int64_t K, uint64_t* has
  * configuration index 0..7 (a configuration that cannot run a shape falls
  * back to the 128x128 tile, index 2); force_splits: 0 = the planner's
  * choice, else the number of K splits (clamped so that no split is empty;
- * the persistent configurations never split); qcols_two_pass: 1 = column
- * quantize passes through the two-pass kernels; int4_direct: 1 = int4 GEMM
- * operands read packed by the direct int4 kernel.  All zero / -1 restores
- * the default.  Errors: I8G_EINVAL for out-of-range values.
+ * the persistent configurations never split); qcols_path: 0 = the
+ * planner's column quantize path, 1 = the two-pass kernels, 2 = the
+ * cooperative one-read kernel wherever the shape allows it (see
+ * quantize_cols); int4_direct: 1 = int4 GEMM operands read packed by the
+ * direct int4 kernel.  All zero / -1 restores the default.  Errors:
+ * I8G_EINVAL for out-of-range values.
  */
-int i8g_set_test_overrides(int32_t force_tile, int32_t force_splits, int32_t qcols_two_pass,
+int i8g_set_test_overrides(int32_t force_tile, int32_t force_splits, int32_t qcols_path,
                            int32_t int4_direct);
 
 /*

@@ -439,14 +439,15 @@ def probe_hash(seed, M, N, K, device=None):
     return h
 
 
-_overrides = {"force_tile": -1, "force_splits": 0, "qcols_two_pass": 0, "int4_direct": 0}
+_overrides = {"force_tile": -1, "force_splits": 0, "qcols_path": 0, "int4_direct": 0}
 
 
 @contextlib.contextmanager
 def plan_overrides(**kw):
     """Plan overrides for tests (i8g_set_test_overrides) inside a with-block:
     force_tile (-1: the planner's choice), force_splits (0: the planner's),
-    qcols_two_pass, int4_direct.  Blocks nest: settings not given are kept
+    qcols_path (0: the planner's, 1: two-pass kernels, 2: cooperative
+    one-read kernel where the shape allows it), int4_direct.  Blocks nest: settings not given are kept
     from the enclosing block, and each block restores the previous ones."""
     unknown = set(kw) - set(_overrides)
     if unknown:
@@ -456,7 +457,7 @@ def plan_overrides(**kw):
     new.update({k: int(v) for k, v in kw.items()})
 
     def apply(o):
-        _check(load().i8g_set_test_overrides(o["force_tile"], o["force_splits"], o["qcols_two_pass"],
+        _check(load().i8g_set_test_overrides(o["force_tile"], o["force_splits"], o["qcols_path"],
                                              o["int4_direct"]))
         _overrides.update(o)
 

@@ -735,15 +735,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Requires K % 64 == 0, K >= 64 * (STAGES - 1) and ldc <= kPersistMaxLdc (the
 // offsets within a 32-row block stay below the record count).
 // ---------------------------------------------------------------------------
-// A pointer the caller knows to be the same in every lane, in scalar
-// registers (a buffer resource built from it then needs no per-lane loop).
-template <class T>
-__device__ __forceinline__ T* uniform_ptr(T* q) {
-  const uint64_t v = reinterpret_cast<uint64_t>(q);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
-}
 
 // LDS byte address of a pointer into __shared__ memory.
 template <class T>
@@ -1899,16 +1890,16 @@ static int device_cus() {
 // Plan overrides set by i8g_set_test_overrides (tests only; the output
 // never depends on the plan).  Read once per plan, never from the
 // environment.
-static std::atomic<int> g_force_tile{-1}, g_force_splits{0}, g_qcols_two_pass{0}, g_int4_direct{0};
+static std::atomic<int> g_force_tile{-1}, g_force_splits{0}, g_qcols_path{0}, g_int4_direct{0};
 
-void set_test_overrides(int force_tile, int force_splits, int qcols_two_pass, int int4_direct) {
+void set_test_overrides(int force_tile, int force_splits, int qcols_path, int int4_direct) {
   g_force_tile.store(force_tile, std::memory_order_relaxed);
   g_force_splits.store(force_splits, std::memory_order_relaxed);
-  g_qcols_two_pass.store(qcols_two_pass, std::memory_order_relaxed);
+  g_qcols_path.store(qcols_path, std::memory_order_relaxed);
   g_int4_direct.store(int4_direct, std::memory_order_relaxed);
 }
 
-bool qcols_two_pass_requested() { return g_qcols_two_pass.load(std::memory_order_relaxed) != 0; }
+int qcols_path_requested() { return g_qcols_path.load(std::memory_order_relaxed); }
 
 constexpr int kCfgInt4 = kNumCfgs;   // gemm_i4_kernel, planned as the 128x128 tile
 

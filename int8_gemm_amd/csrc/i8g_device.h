@@ -14,6 +14,16 @@
 
 namespace i8g {
 
+// A pointer the caller knows to be the same in every lane, in scalar
+// registers (a buffer resource built from it then needs no per-lane loop).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // RN(1e-8): the scale floor of step 1, bit pattern 0x322BCC77.
 __device__ __forceinline__ float scale_floor() { return __uint_as_float(0x322BCC77u); }
 

@@ -87,10 +87,11 @@ hipError_t launch_widen_int4(const int8_t* P, int64_t ldp, int64_t rows, int64_t
                              hipStream_t stream);
 bool int4_direct_requested();
 // Test overrides (i8g_set_test_overrides): forced tile configuration (-1:
-// none) and split count (0: none), column quantize through the two-pass
-// kernels, int4 operands through gemm_i4_kernel.  Process-wide.
-void set_test_overrides(int force_tile, int force_splits, int qcols_two_pass, int int4_direct);
-bool qcols_two_pass_requested();
+// none) and split count (0: none), column quantize path (0: the planner's,
+// 1: the two-pass kernels, 2: the cooperative one-read kernel where the
+// shape allows it), int4 operands through gemm_i4_kernel.  Process-wide.
+void set_test_overrides(int force_tile, int force_splits, int qcols_path, int int4_direct);
+int qcols_path_requested();
 // Requantizing epilogue: one K split, a non-persistent tile (a forced tile
 // 0..2 honoured for tests); the workspace adds M words of row maxima.
 GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K);

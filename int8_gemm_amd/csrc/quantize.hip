@@ -329,6 +329,270 @@ qcols_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
 }
 
 // ---------------------------------------------------------------------------
+// cols, one read of X for large inputs (cooperative launch).  A band is 32
+// columns: one 128-byte line of every row.  The band's rows are split into
+// chunks of 1024 rows, one per member of a group of P workgroups (512
+// threads each, a lane holding 16 rows x 4 columns in registers); the
+// members of a group sit on one XCD (workgroup ids are dealt to the 8 XCDs
+// round-robin) and walk the same bands.  Per band a member
+//  1. reads its chunk with whole-line loads and reduces its 32 column maxima;
+//  2. raises scale[j] to its partial scale max(RN(a/127), RN(1e-8)) with an
+//     agent-scope atomicMax on the bit pattern (RN and the floor are
+//     monotone and positive floats order like their bits, so the largest
+//     partial scale is the scale of the column max, in any order); it waits
+//     for the atomics' returned values, so they have been performed;
+//  3. adds 1 to the band's counter (agent scope) and waits, with a bounded
+//     spin, until all P members have added theirs: every partial maximum is
+//     then in place, and the final scales are read with agent-scope atomic
+//     loads;
+//  4. quantizes its chunk, transposes it through LDS and stores 32 segments
+//     of 1024 bytes of Qt.
+// The counter lives in the first four bytes of the band's first Qt row,
+// zeroed by qcols_coop_init_kernel: those bytes belong to member 0, which
+// writes their codes (an atomic exchange) only after the other members have
+// left the wait (each adds 1 more, so the count reaches 2P-1).  All waits
+// are bounded; a member whose wait times out (the grid was not resident)
+// stops waiting for the rest of the launch and leaves the band's scales NaN.
+// Requires rows % 256 == 0, rows >= 1024, cols % 32 == 0, X and Qt 16-byte
+// aligned, ldx % 4 == 0, ldqt % 16 == 0 and 1024 rows of X addressable with
+// 32-bit offsets.
+// ---------------------------------------------------------------------------
+constexpr int QK_THREADS = 512;            // 8 waves
+constexpr int QK_ROWS = 1024;              // rows of X per member and band
+constexpr int QK_COLS = 32;                // columns per band (128 bytes of a row)
+constexpr int QK_TS = QK_ROWS / 4 + 4;     // words per LDS tile row (padded)
+constexpr unsigned int kQkWaitLimit = 1u << 20;   // spins of ~64 cycles: tens of ms
+constexpr double kQkMinBytes = 256.0 * 1024 * 1024;   // X bytes from which the path is used
+
+template <int FMT>
+__global__ void qcols_coop_init_kernel(float* scale, int64_t cols, int8_t* Qt, int64_t ldqt,
+                                       int64_t nbands) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < cols) scale[i] = scale_of_absmax_fmt<FMT>(0.0f);   // the (rounded) floor
+  if (i < nbands) *reinterpret_cast<unsigned int*>(Qt + i * QK_COLS * ldqt) = 0u;
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(QK_THREADS, 4)
+qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                  int8_t* __restrict__ Qt, int64_t ldqt, float* __restrict__ scale, int P, int NG,
+                  int64_t nbands) {
+  __shared__ float red[8][QK_COLS];
+  __shared__ float s_inv[QK_COLS];
+  __shared__ int s_ok;
+  __shared__ __attribute__((aligned(16))) unsigned int tile[QK_COLS][QK_TS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int slot = t & 7, rg = t >> 3;                 // 16-byte slot of the line, row group
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int m = q % P, g = xcd + 8 * (q / P);          // member m of group g
+  if (g >= NG) return;
+  const int64_t r0 = (int64_t)m * QK_ROWS;
+  // 256-row blocks of this chunk inside X (workgroup-uniform)
+  const int nblk = __builtin_amdgcn_readfirstlane((int)((rows - r0) / 256 < 4 ? (rows - r0) / 256 : 4));
+  const int ld4 = (int)(ldx * 4);
+  const int vo = (4 * rg) * ld4 + slot * 16;           // rows 4*rg + e + 256*i of the chunk
+  bool timed_out = false;
+  unsigned int* pend_addr = nullptr;                   // member 0's counter word, codes pending
+  unsigned int pend_codes = 0;
+  auto settle = [&](bool block) __attribute__((always_inline)) {
+    if (t != 0 || pend_addr == nullptr) return;
+    unsigned int n = 0;
+    while (__hip_atomic_load(pend_addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           (unsigned int)(2 * P - 1)) {
+      if (!block && n >= 64) return;                   // again after the next band
+      __builtin_amdgcn_s_sleep(2);
+      if (++n > kQkWaitLimit) break;
+    }
+    __hip_atomic_exchange(pend_addr, pend_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pend_addr = nullptr;
+  };
+  for (int64_t b = g; b < nbands; b += NG) {
+    // 1. the chunk in registers: buffer loads from a uniform base, one 32-bit
+    // offset per lane, uniform row offsets; blocks past the end of X skipped
+    float4 v[16];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(uniform_ptr(X + r0 * ldx + b * QK_COLS)), 0, 0x7FFFFFF0, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        if (i < nblk) {
+          const v4f x = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (e + 256 * i) * ld4, 0));
+          v[i * 4 + e] = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          v[i * 4 + e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      m0 = fmaxf(m0, fabsf(v[i].x));
+      m1 = fmaxf(m1, fabsf(v[i].y));
+      m2 = fmaxf(m2, fabsf(v[i].z));
+      m3 = fmaxf(m3, fabsf(v[i].w));
+    }
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {            // lanes with the same slot
+      m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+      m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+      m2 = fmaxf(m2, __shfl_xor(m2, off, 64));
+      m3 = fmaxf(m3, __shfl_xor(m3, off, 64));
+    }
+    if (lane < 8) {
+      red[wave][slot * 4 + 0] = m0;
+      red[wave][slot * 4 + 1] = m1;
+      red[wave][slot * 4 + 2] = m2;
+      red[wave][slot * 4 + 3] = m3;
+    }
+    __syncthreads();
+    unsigned int* const counter = reinterpret_cast<unsigned int*>(Qt + b * QK_COLS * ldqt);
+    unsigned int* const sbits = reinterpret_cast<unsigned int*>(scale) + b * QK_COLS;
+    if (t < QK_COLS) {
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) a = fmaxf(a, red[w][t]);
+      // 2. the partial scale into scale[j]; the returned value is consumed
+      const unsigned int old = __hip_atomic_fetch_max(sbits + t, __float_as_uint(scale_of_absmax_fmt<FMT>(a)),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("" ::"v"(old));
+    }
+    __builtin_amdgcn_s_waitcnt(0);                      // this lane's maximum has returned
+    __syncthreads();                                    // ... and every lane's
+    // 3. arrive, wait for the group, leave
+    if (t == 0) {
+      const unsigned int mine = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("" ::"v"(mine));
+      bool ok;
+      if (!timed_out) {
+        unsigned int n = 0;
+        ok = true;
+        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned int)P) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++n > kQkWaitLimit) {
+            ok = false;
+            break;
+          }
+        }
+      } else {
+        ok = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned int)P;
+      }
+      timed_out = timed_out || !ok;
+      s_ok = ok ? 1 : 0;
+      if (m != 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (t < QK_COLS) {
+      const float s = __uint_as_float(__hip_atomic_load(sbits + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (!s_ok) __hip_atomic_exchange(sbits + t, 0x7FC00000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_inv[t] = recip_rn(s);
+    }
+    __syncthreads();
+    // 4. quantize, transpose through LDS (4 consecutive rows per word), store
+    const float i0 = s_inv[slot * 4], i1 = s_inv[slot * 4 + 1], i2 = s_inv[slot * 4 + 2], i3 = s_inv[slot * 4 + 3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unsigned int w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 x = v[i * 4 + e];
+        w0 |= ((unsigned int)quantize1(x.x, i0) & 0xFFu) << (8 * e);
+        w1 |= ((unsigned int)quantize1(x.y, i1) & 0xFFu) << (8 * e);
+        w2 |= ((unsigned int)quantize1(x.z, i2) & 0xFFu) << (8 * e);
+        w3 |= ((unsigned int)quantize1(x.w, i3) & 0xFFu) << (8 * e);
+      }
+      tile[slot * 4 + 0][rg + 64 * i] = w0;
+      tile[slot * 4 + 1][rg + 64 * i] = w1;
+      tile[slot * 4 + 2][rg + 64 * i] = w2;
+      tile[slot * 4 + 3][rg + 64 * i] = w3;
+    }
+    __syncthreads();
+    {
+      const int jj = t >> 4, part = t & 15;             // Qt row b*32+jj, bytes part*64 .. +64
+      int8_t* dst = Qt + (b * QK_COLS + jj) * ldqt + r0 + part * 64;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int w = part * 16 + qq * 4;
+        if (r0 + part * 64 + qq * 16 < rows) {           // rows % 256 == 0: whole 16-byte groups
+          const unsigned int a0 = tile[jj][w], a1 = tile[jj][w + 1], a2 = tile[jj][w + 2], a3 = tile[jj][w + 3];
+          if (m == 0 && jj == 0 && part == 0 && qq == 0) {
+            settle(true);                                // the previous band's word first
+            unsigned int* d = reinterpret_cast<unsigned int*>(dst);
+            d[1] = a1;
+            d[2] = a2;
+            d[3] = a3;
+            pend_addr = d;                               // d[0] is the counter
+            pend_codes = a0;
+          } else {
+            *reinterpret_cast<uint4*>(dst + qq * 16) = make_uint4(a0, a1, a2, a3);
+          }
+        }
+      }
+    }
+    settle(false);
+    __syncthreads();                                    // LDS is reused by the next band
+  }
+  settle(true);
+}
+
+// Eligibility of the cooperative path for a column pass (see above).
+static bool qcols_coop_shape_ok(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Qt,
+                                int64_t ldqt, int fmt) {
+  return (fmt & FMT_INT4) == 0 && rows >= QK_ROWS && rows % 256 == 0 && cols % QK_COLS == 0 && cols > 0 &&
+         ldx % 4 == 0 && ((uintptr_t)X % 16) == 0 && ((uintptr_t)Qt % 16) == 0 && ldqt % 16 == 0 &&
+         ldx * 4 * QK_ROWS < 0x7FFFFFF0LL;
+}
+
+static bool qcols_takes_coop(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Qt,
+                             int64_t ldqt, int fmt) {
+  const int path = qcols_path_requested();
+  if (path == 1 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
+  return path == 2 || (double)rows * (double)cols * 4.0 >= kQkMinBytes;
+}
+
+// Workgroups of qcols_coop_kernel<FMT> resident per CU on the current device
+// (cached per device).
+template <int FMT>
+static int qcols_coop_occupancy() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, qcols_coop_kernel<FMT>, QK_THREADS, 0) != hipSuccess)
+      n = 0;
+    cache[dev] = n > 0 ? n : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
+// Enqueues the cooperative path; an error means nothing but the (harmless)
+// init kernel ran, and the caller takes another path.
+template <int FMT>
+static hipError_t launch_qcols_coop(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* Qt,
+                                    int64_t ldqt, float* scale, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return hipErrorInvalidDevice;
+  const int occ = qcols_coop_occupancy<FMT>();
+  const int P = (int)((rows + QK_ROWS - 1) / QK_ROWS);
+  const int64_t nbands = cols / QK_COLS;
+  const int64_t cap_groups = ((int64_t)cus * occ / P) / 8 * 8;   // resident groups, a multiple of 8
+  if (occ <= 0 || cap_groups < 8) return hipErrorCooperativeLaunchTooLarge;
+  const int64_t NG = nbands < cap_groups ? (nbands + 7) / 8 * 8 : cap_groups;
+  hipLaunchKernelGGL(qcols_coop_init_kernel<FMT>, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0,
+                     stream, scale, cols, Qt, ldqt, nbands);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int p = P, ng = (int)NG;
+  void* args[] = {&X, &rows, &cols, &ldx, &Qt, &ldqt, &scale, &p, &ng, const_cast<int64_t*>(&nbands)};
+  e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(qcols_coop_kernel<FMT>), dim3((unsigned int)(NG * P)),
+                                 dim3(QK_THREADS), args, 0, stream);
+  return e;
+}
+
+// ---------------------------------------------------------------------------
 // cols, one kernel (rows <= 8192): a 1024-thread workgroup owns a band of BC
 // columns and every row, holding the band in registers (at most 32 floats
 // per thread), so X is read from HBM once.  The column maxima are reduced
@@ -486,10 +750,14 @@ hipError_t quantize_cols_int8(const float* X, int64_t rows, int64_t cols, int64_
                               int8_t* Qt, int64_t ldqt, float* scale, hipStream_t stream) {
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Qt % 16 == 0) && (ldqt % 16 == 0);
+  if (qcols_takes_coop(X, rows, cols, ldx, Qt, ldqt, FMT)) {
+    if (launch_qcols_coop<FMT>(X, rows, cols, ldx, Qt, ldqt, scale, stream) == hipSuccess) return hipSuccess;
+    (void)hipGetLastError();   // the cooperative launch was refused: the paths below
+  }
   int bc = rows > 0 ? qcols_band(rows, cols) : 0;
-  // the test override forces the two-pass kernels (the bytes never depend
-  // on the path)
-  if (qcols_two_pass_requested()) bc = 0;
+  // the test override can force the two-pass kernels (the bytes never
+  // depend on the path)
+  if (qcols_path_requested() == 1) bc = 0;
   if (bc > 0) {
     const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
     switch (bc) {
@@ -607,7 +875,7 @@ hipError_t quantize_cols_int4(const float* X, int64_t rows, int64_t cols, int64_
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   // up to 8192 rows: the one-kernel band path, packing as it stores
   int bc = rows > 0 ? qcols_band(rows, cols) : 0;
-  if (qcols_two_pass_requested()) bc = 0;
+  if (qcols_path_requested() == 1) bc = 0;
   if (bc > 0) {
     const dim3 grid((unsigned int)((cols + bc - 1) / bc)), block(QCR_THREADS);
     switch (bc) {
@@ -731,7 +999,8 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
   }
   q.vec_out = ((uintptr_t)Q % 16 == 0) && (ldq % 16 == 0);
   const int bc = qcols_band(rows, cols);
-  if (bc == 0 || qcols_two_pass_requested()) return false;   // the multi-kernel path
+  if (bc == 0 || qcols_path_requested() == 1) return false;   // the multi-kernel path
+  if (qcols_takes_coop(X, rows, cols, ldx, Q, ldq, fmt)) return false;   // a launch of its own
   q.kind = QK_COLS_REG; q.param = bc;
   q.blocks = (int)((cols + bc - 1) / bc);
   return true;

@@ -200,7 +200,7 @@ def test_int4_columns_both_paths(g, fmt, two_pass, shape):
     rows, cols = shape
     say("int4 cols", fmt, "two_pass", two_pass, rows, cols)
     X = _data(rows + cols + fmt, rows, cols)
-    with g.plan_overrides(qcols_two_pass=two_pass):
+    with g.plan_overrides(qcols_path=1 if two_pass else 0):
         Qt, st = g.quantize_cols_fmt(torch.from_numpy(X).cuda(), fmt)
         torch.cuda.synchronize()
     qc, sc = F.quantize_cols(X, fmt)

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from oracle import adversarial, hashref, ref
+from oracle import formats as F
 from synth import inputs as S
 from tests.parity import assert_bits, check_against_oracle
 
@@ -115,12 +116,73 @@ def test_quantize_cols_two_pass(g, rows, cols):
     scales, then quantize-transpose) on every shape, forced."""
     say("quantize_cols two-pass", rows, cols)
     X = np.ascontiguousarray(_quant_input(cols, rows, rows * 7919 + cols + 1).T)
-    with g.plan_overrides(qcols_two_pass=True):
+    with g.plan_overrides(qcols_path=1):
         Qt, s = g.quantize_cols(to_dev(X))
         torch.cuda.synchronize()
     Qo, so = ref.quantize_cols(X)
     assert_bits(Qt.cpu().numpy(), Qo, "Qt")
     assert_bits(s.cpu().numpy(), so, "scale")
+
+
+# shapes the cooperative one-read column kernel takes (rows a multiple of
+# 256, at least 1024; columns a multiple of 32): one member per band, several
+# members with a partial last chunk, more bands than resident groups
+COOP_SHAPES = [(1024, 32), (1280, 96), (3072, 768), (2048, 4096), (8192, 800), (4352, 6400)]
+
+
+@pytest.mark.parametrize("rows,cols", COOP_SHAPES)
+def test_quantize_cols_cooperative(g, rows, cols):
+    """The cooperative column kernel (partial maxima exchanged between the
+    workgroups of a band, counter in the band's first Qt bytes), forced on
+    shapes below its size threshold, against the oracle; also with
+    power-of-two scales."""
+    say("quantize_cols cooperative", rows, cols)
+    X = np.ascontiguousarray(_quant_input(cols, rows, rows * 31 + cols).T)
+    X[:, 3] = 0
+    dX = to_dev(X)
+    with g.plan_overrides(qcols_path=2):
+        Qt, s = g.quantize_cols(dX)
+        Qp, sp = g.quantize_cols_fmt(dX, g.FMT_POW2)
+        torch.cuda.synchronize()
+    Qo, so = ref.quantize_cols(X)
+    assert_bits(Qt.cpu().numpy(), Qo, "Qt")
+    assert_bits(s.cpu().numpy(), so, "scale")
+    Qpo, spo = F.quantize_cols(X, F.POW2)
+    assert_bits(Qp.cpu().numpy(), Qpo, "Qt pow2")
+    assert_bits(sp.cpu().numpy(), spo, "scale pow2")
+
+
+def test_quantize_cols_cooperative_graph_replays(g):
+    """The cooperative launch captured in a HIP graph: every replay, with
+    eager work between replays, writes the oracle's bytes."""
+    rows, cols = 4096, 1024
+    X = np.ascontiguousarray(_quant_input(cols, rows, 4242).T)
+    Qo, so = ref.quantize_cols(X)
+    dX = to_dev(X)
+    Qt = torch.empty((cols, rows), dtype=torch.int8, device="cuda")
+    s = torch.empty(cols, dtype=torch.float32, device="cuda")
+    lib = g.load()
+
+    def call():
+        st = torch.cuda.current_stream().cuda_stream
+        assert lib.quantize_cols(dX.data_ptr(), rows, cols, cols, Qt.data_ptr(), rows, s.data_ptr(), st) == 0
+
+    say("quantize_cols cooperative in a graph")
+    with g.plan_overrides(qcols_path=2):
+        call()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        for it in range(3):
+            Qt.fill_(5)
+            s.fill_(-1.0)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert_bits(Qt.cpu().numpy(), Qo, f"Qt replay {it}")
+            assert_bits(s.cpu().numpy(), so, f"scale replay {it}")
+            call()
+            torch.cuda.synchronize()
 
 
 def test_quantize_cols_unaligned(g):
