@@ -142,7 +142,7 @@ int enqueue_gemm(const int8_t* QA, int64_t lda, const float* s_row, const int8_t
   p.k_per_split = plan.k_per_split;
   p.relu = (flags & I8G_RELU) ? 1 : 0;
   p.do_hash = want_hash ? 1 : 0;
-  p.stream_out = ((double)M * (double)N * 4.0 > 128.0 * 1024 * 1024) ? 1 : 0;
+  p.stream_out = ((double)M * (double)N * 4.0 > kStreamOutBytes) ? 1 : 0;
   char* ws = reinterpret_cast<char*>(workspace);
   p.ticket = reinterpret_cast<unsigned int*>(ws);
   p.hash_parts = reinterpret_cast<unsigned long long*>(ws + kWsHeader);

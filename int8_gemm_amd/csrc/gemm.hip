@@ -743,9 +743,16 @@ __device__ __forceinline__ uint32_t lds_addr(const T* q) {
 }
 
 constexpr unsigned int kBufRecords = 0x7FFFFFF0u;   // record count of the output resource
+// Cache policy of the output stores for outputs larger than half the
+// last-level cache (GemmParams::stream_out): the nontemporal bit.  Measured
+// on the LM-head forward (1.65 GB of f32 output written while the operands
+// stream through L2): ~700 us with ordinary stores, ~425 us with this bit,
+// ~360 us with the stores dropped altogether; ordinary stores keep a smaller
+// output in the last-level cache for the kernel that reads it next.
+constexpr int kStoreNT = 2;
 constexpr int kBufInvalid = 0x7FFFFFF0;             // voffset of a dropped store
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool RELU>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool RELU, bool NTSTORE>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 gemm_i8_persist_kernel(const GemmParams p) {
   constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
@@ -974,7 +981,7 @@ gemm_i8_persist_kernel(const GemmParams p) {
           const int soff = (q * 8 + e) * (int)ldc4;
           int vo = o.voff[j];
           if (R) vo = (q * 8 + e) < lim ? vo : kBufInvalid;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, vo, soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, vo, soff, NTSTORE ? kStoreNT : 0);
         }
       }
     };
@@ -1191,7 +1198,7 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU, int STAGES, int WPC>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU, int STAGES, int WPC, bool NTSTORE>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WPC)
 gemm_i8_persist128_kernel(const GemmParams p) {
   constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
@@ -1468,7 +1475,8 @@ gemm_i8_persist128_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = e0; e < e0 + 2; ++e) {
         tcol[j] += (uint64_t)(unsigned int)d.rk[q % 2][e] * (uint64_t)__float_as_uint(xq[e]);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xq[e]), rsrc, o.voff[j], (q * 8 + e) * (int)ldc4, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xq[e]), rsrc, o.voff[j], (q * 8 + e) * (int)ldc4,
+                                              NTSTORE ? kStoreNT : 0);
       }
       if constexpr (st == 4) asm volatile("" : "+v"(tcol[j]));
     }
@@ -1721,7 +1729,8 @@ gemm_i8_persist128_kernel(const GemmParams p) {
       const int rr = (v >> 2) * 8 + (v & 3);
       float y = epilogue1(acc0[i][j][v], srp[rr], sc);
       if (RELU) y = relu_pos0(y);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, out_cur.voff[j], rr * (int)ldc4, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rsrc, out_cur.voff[j], rr * (int)ldc4,
+                                            NTSTORE ? kStoreNT : 0);
     }
   };
   // The share store and the ticket are issued by every lane of every wave,
@@ -1856,18 +1865,19 @@ struct TileCfg {
   double wg_macs;        // MAC/s of one resident workgroup in its main loop
   double wg_out_bw;      // bytes/s of output one workgroup writes in its epilogue
   double tile_overhead;  // persistent: seconds per tile beyond its MACs
+  double tile_overhead_nt;  // the same with nontemporal output stores (outputs > 128 MB)
   bool persistent;       // one workgroup per CU walking tiles, epilogue drained under the next tile
   int kstage;            // bytes of K per LDS stage
 };
 static const TileCfg kCfgs[] = {
-    {256, 256, 1, 4.5e12, 20e9, 0, false, 64},    // eight waves (two per SIMD), 128x64 each
-    {256, 128, 1, 3.3e12, 9.8e9, 0, false, 64},   // four waves, 128x64 each
-    {128, 128, 2, 1.43e12, 6.9e9, 0, false, 64},  // four waves, 64x64 each
-    {256, 256, 1, 4.0e12, 20e9, 0, false, 64},    // four waves, 128x128 each (tests only)
-    {256, 128, 1, 3.0e12, 0, 6.0e-6, true, 64},   // persistent, 128x64 per wave (tests only)
-    {128, 192, 1, 3.0e12, 0, 5.2e-6, true, 64},   // persistent, four waves, 64x96 each
-    {128, 192, 1, 3.7e12, 0, 5.5e-6, true, 128},  // persistent, 128-byte stages, 64x96 per wave
-    {128, 128, 2, 1.75e12, 0, 4.5e-6, true, 128}, // the same, 64x64 per wave, two workgroups per CU
+    {256, 256, 1, 4.5e12, 20e9, 0, 0, false, 64},    // eight waves (two per SIMD), 128x64 each
+    {256, 128, 1, 3.3e12, 9.8e9, 0, 0, false, 64},   // four waves, 128x64 each
+    {128, 128, 2, 1.43e12, 6.9e9, 0, 0, false, 64},  // four waves, 64x64 each
+    {256, 256, 1, 4.0e12, 20e9, 0, 0, false, 64},    // four waves, 128x128 each (tests only)
+    {256, 128, 1, 3.0e12, 0, 6.0e-6, 6.0e-6, true, 64},   // persistent, 128x64 per wave (tests only)
+    {128, 192, 1, 3.0e12, 0, 5.2e-6, 5.2e-6, true, 64},   // persistent, four waves, 64x96 each
+    {128, 192, 1, 3.7e12, 0, 5.5e-6, 2.1e-6, true, 128},  // persistent, 128-byte stages, 64x96 per wave
+    {128, 128, 2, 1.75e12, 0, 4.5e-6, 1.3e-6, true, 128}, // the same, 64x64 per wave, two workgroups per CU
 };
 constexpr int kNumCfgs = kNumGemmCfgs;
 static_assert(sizeof(kCfgs) / sizeof(kCfgs[0]) == kNumCfgs, "one entry per configuration");
@@ -1921,6 +1931,9 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
   GemmPlan best{};
   if (M <= 0 || N <= 0) return best;
   const int cus = device_cus();
+  // outputs above half the last-level cache are written with nontemporal
+  // stores (the launch sets GemmParams::stream_out by the same rule)
+  const bool stream_out = (double)M * (double)N * 4.0 > kStreamOutBytes;
   // Estimated seconds (see TileCfg), plus the split-K partial round trip;
   // no plan beats the whole output written at ~5 TB/s.
   const double mem_bw = 4.0e12;
@@ -1947,9 +1960,12 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
       // rounds of tiles (MLP up-projection 8192x3072x768: 35 against 38 us);
       // slower on the LM head's 50 rounds at K = 768 (706 against ~680 us
       // for tile 0) and its K = 8192 weight gradient (375 against ~355 us)
-      if (t.per_cu > 1 && force_tile < 0 && (K > 1024 || tiles > 8 * grid)) continue;
+      // (with nontemporal stores, for outputs above 128 MB, it also wins on
+      // many rounds: LM-head forward ~425 us against ~680 for tile 0)
+      if (t.per_cu > 1 && force_tile < 0 && (K > 1024 || (tiles > 8 * grid && !stream_out))) continue;
       const double rounds = std::ceil((double)tiles / (double)grid);
-      double cost = rounds * ((double)t.bm * t.bn * K / t.wg_macs + t.tile_overhead);
+      double cost = rounds * ((double)t.bm * t.bn * K / t.wg_macs +
+                              (stream_out ? t.tile_overhead_nt : t.tile_overhead));
       const double wr = (double)M * N * 4 / write_bw;
       if (wr > cost) cost = wr;
       if (cost < best_cost * 0.999) {
@@ -2018,6 +2034,29 @@ GemmPlan plan_gemm_forced(int64_t M, int64_t N, int64_t K, bool allow_persistent
   return best;
 }
 
+// Persistent kernels: the ReLU and store-policy variants of one tile.
+template <int BM, int BN>
+static void launch_persist(const GemmParams& p, unsigned int grid, hipStream_t stream) {
+  if (p.relu) {
+    if (p.stream_out) hipLaunchKernelGGL((gemm_i8_persist_kernel<BM, BN, 2, 2, 4, true, true>), dim3(grid), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_i8_persist_kernel<BM, BN, 2, 2, 4, true, false>), dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    if (p.stream_out) hipLaunchKernelGGL((gemm_i8_persist_kernel<BM, BN, 2, 2, 4, false, true>), dim3(grid), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_i8_persist_kernel<BM, BN, 2, 2, 4, false, false>), dim3(grid), dim3(256), 0, stream, p);
+  }
+}
+
+template <int BM, int BN, int STAGES, int WPC>
+static void launch_persist128(const GemmParams& p, unsigned int grid, hipStream_t stream) {
+  if (p.relu) {
+    if (p.stream_out) hipLaunchKernelGGL((gemm_i8_persist128_kernel<BM, BN, 2, 2, true, STAGES, WPC, true>), dim3(grid), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_i8_persist128_kernel<BM, BN, 2, 2, true, STAGES, WPC, false>), dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    if (p.stream_out) hipLaunchKernelGGL((gemm_i8_persist128_kernel<BM, BN, 2, 2, false, STAGES, WPC, true>), dim3(grid), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_i8_persist128_kernel<BM, BN, 2, 2, false, STAGES, WPC, false>), dim3(grid), dim3(256), 0, stream, p);
+  }
+}
+
 hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t stream) {
   const unsigned int grid = (unsigned int)plan.grid;
   switch (plan.cfg) {
@@ -2034,16 +2073,10 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
       hipLaunchKernelGGL((gemm_i8_dma_kernel<256, 256, 2, 2, 4>), dim3(grid), dim3(256), 0, stream, p);
       break;
     case 4:
-      if (p.relu)
-        hipLaunchKernelGGL((gemm_i8_persist_kernel<256, 128, 2, 2, 4, true>), dim3(grid), dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((gemm_i8_persist_kernel<256, 128, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
+      launch_persist<256, 128>(p, grid, stream);
       break;
     case 5:
-      if (p.relu)
-        hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, true>), dim3(grid), dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((gemm_i8_persist_kernel<128, 192, 2, 2, 4, false>), dim3(grid), dim3(256), 0, stream, p);
+      launch_persist<128, 192>(p, grid, stream);
       break;
     case kCfgInt4:
       if (p.a4 && p.b4)
@@ -2054,16 +2087,10 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
         hipLaunchKernelGGL((gemm_i4_kernel<128, 128, 2, 2, false, true>), dim3(grid), dim3(256), 0, stream, p);
       break;
     case 7:
-      if (p.relu)
-        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 128, 2, 2, true, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 128, 2, 2, false, 2, 2>), dim3(grid), dim3(256), 0, stream, p);
+      launch_persist128<128, 128, 2, 2>(p, grid, stream);
       break;
     default:
-      if (p.relu)
-        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, true, 3, 1>), dim3(grid), dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((gemm_i8_persist128_kernel<128, 192, 2, 2, false, 3, 1>), dim3(grid), dim3(256), 0, stream, p);
+      launch_persist128<128, 192, 3, 1>(p, grid, stream);
       break;
   }
   if (plan.splits > 1)

@@ -53,6 +53,11 @@ struct GemmPlan {
 // offsets; larger leading dimensions are planned without it.
 constexpr int64_t kPersistMaxLdc = int64_t(1) << 23;
 
+// Outputs larger than this (half of the 256 MB last-level cache) are stored
+// with nontemporal hints (GemmParams::stream_out); smaller ones stay in the
+// cache for the kernel that reads them next.
+constexpr double kStreamOutBytes = 128.0 * 1024 * 1024;
+
 // Number of tile configurations of the planner (indices 0 .. kNumGemmCfgs-1;
 // kNumGemmCfgs itself denotes the direct int4 kernel).
 constexpr int kNumGemmCfgs = 8;

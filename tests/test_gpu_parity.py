@@ -288,6 +288,23 @@ def test_persistent128_kernel(g, tile):
             check_against_oracle(got, A, B, relu)
 
 
+@pytest.mark.parametrize("tile", [5, 6, 7])
+def test_persistent_nontemporal_stores(g, tile):
+    """An output above 128 MB is written with nontemporal stores by the
+    persistent kernels: ragged N, ReLU, several tiles per workgroup, every
+    byte and the hash against the oracle."""
+    M, N, K = 4096, 8200, 768                   # 134 MB of f32 output
+    rng = np.random.default_rng(700 + tile)
+    A = rng.standard_t(3, (M, K)).astype(F32)
+    B = rng.standard_normal((K, N)).astype(F32)
+    A[rng.random(M) < 0.02] = 0
+    with g.plan_overrides(force_tile=tile):
+        assert g.plan_query(M, N, K) == (tile, 1), "the forced plan did not run"
+        say("nontemporal persistent tile", tile, "MNK", M, N, K)
+        got = run_method(g, A, B, relu=True)
+    check_against_oracle(got, A, B, True)
+
+
 def test_w2_mlp_full_size(g):
     """MLP up-projection (ReLU) and the down-projection on its output, full
     size, every output byte."""
