@@ -593,7 +593,7 @@ def lm_head_record(g, torch, args, scrub):
            "tops": round(ops / (ms * 1e-3) / 1e12, 1),
            "pct_of_int8_peak": round(100.0 * ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
            "launch": launch,
-           "gemms": [k for k in kernels if k["call"].endswith(".gemm")],
+           "gemms": [dict(k, traffic=traffic_for(k["call"])) for k in kernels if k["call"].endswith(".gemm")],
            "quantize": [k for k in kernels if not k["call"].endswith(".gemm")],
            "quantize_batch": batch,
            "parity": stored == want and fused == want,
