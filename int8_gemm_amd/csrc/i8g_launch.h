@@ -93,8 +93,9 @@ hipError_t launch_widen_int4(const int8_t* P, int64_t ldp, int64_t rows, int64_t
 bool int4_direct_requested();
 // Test overrides (i8g_set_test_overrides): forced tile configuration (-1:
 // none) and split count (0: none), column quantize path (0: the planner's,
-// 1: the two-pass kernels, 2: the cooperative one-read kernel where the
-// shape allows it), int4 operands through gemm_i4_kernel.  Process-wide.
+// 1: the two-pass kernels, 2: the cooperative one-read kernel, 3: the two
+// whole-line passes, where the shape allows them), int4 operands through
+// gemm_i4_kernel.  Process-wide.
 void set_test_overrides(int force_tile, int force_splits, int qcols_path, int int4_direct);
 int qcols_path_requested();
 // Requantizing epilogue: one K split, a non-persistent tile (a forced tile

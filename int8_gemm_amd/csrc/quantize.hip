@@ -535,6 +535,124 @@ qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
   settle(true);
 }
 
+// ---------------------------------------------------------------------------
+// cols, two passes over whole lines (medium inputs, no cross-workgroup wait).
+// The same bands and chunks as qcols_coop_kernel, as two launches after
+// qcols_init_kernel has set every scale to the floor:
+//  1. qcols_lines_max_kernel: each workgroup (band, chunk) reads its chunk
+//     with whole-line loads and raises the band's 32 scales to its partial
+//     scales (atomicMax on the bit patterns; the largest partial scale is the
+//     scale of the column max);
+//  2. qcols_lines_quant_kernel: each workgroup reads its chunk again (an
+//     input of up to a few hundred MB is still in the 256 MB last-level
+//     cache), reads the final scales, quantizes and stores the transposed
+//     chunk.
+// Same requirements as the cooperative path.
+// ---------------------------------------------------------------------------
+// The chunk of (band b, rows r0 .. r0+1023) in registers: lane (slot, rg)
+// holds rows 4*rg + e + 256*i, columns 4*slot .. 4*slot+3 of the band
+// (v[4*i + e]); 256-row blocks past the end of X are zeros.
+__device__ __forceinline__ void qk_load_chunk(const float* X, int64_t ldx, int64_t r0, int64_t b, int nblk,
+                                              int vo, int ld4, float4 (&v)[16]) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(uniform_ptr(X + r0 * ldx + b * QK_COLS)), 0, 0x7FFFFFF0, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      if (i < nblk) {
+        const v4f x = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (e + 256 * i) * ld4, 0));
+        v[i * 4 + e] = make_float4(x[0], x[1], x[2], x[3]);
+      } else {
+        v[i * 4 + e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(QK_THREADS, 4)
+qcols_lines_max_kernel(const float* __restrict__ X, int64_t rows, int64_t ldx, float* __restrict__ scale, int P) {
+  __shared__ float red[8][QK_COLS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int slot = t & 7, rg = t >> 3;
+  const int64_t b = blockIdx.x / P, r0 = (int64_t)(blockIdx.x % P) * QK_ROWS;
+  const int nblk = __builtin_amdgcn_readfirstlane((int)((rows - r0) / 256 < 4 ? (rows - r0) / 256 : 4));
+  const int ld4 = (int)(ldx * 4);
+  float4 v[16];
+  qk_load_chunk(X, ldx, r0, b, nblk, (4 * rg) * ld4 + slot * 16, ld4, v);
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m0 = fmaxf(m0, fabsf(v[i].x));
+    m1 = fmaxf(m1, fabsf(v[i].y));
+    m2 = fmaxf(m2, fabsf(v[i].z));
+    m3 = fmaxf(m3, fabsf(v[i].w));
+  }
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+    m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+    m2 = fmaxf(m2, __shfl_xor(m2, off, 64));
+    m3 = fmaxf(m3, __shfl_xor(m3, off, 64));
+  }
+  if (lane < 8) {
+    red[wave][slot * 4 + 0] = m0;
+    red[wave][slot * 4 + 1] = m1;
+    red[wave][slot * 4 + 2] = m2;
+    red[wave][slot * 4 + 3] = m3;
+  }
+  __syncthreads();
+  if (t < QK_COLS) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) a = fmaxf(a, red[w][t]);
+    atomicMax(reinterpret_cast<unsigned int*>(scale) + b * QK_COLS + t, __float_as_uint(scale_of_absmax_fmt<FMT>(a)));
+  }
+}
+
+__global__ void __launch_bounds__(QK_THREADS, 4)
+qcols_lines_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t ldx, int8_t* __restrict__ Qt,
+                         int64_t ldqt, const float* __restrict__ scale, int P) {
+  __shared__ float s_inv[QK_COLS];
+  __shared__ __attribute__((aligned(16))) unsigned int tile[QK_COLS][QK_TS];
+  const int t = threadIdx.x;
+  const int slot = t & 7, rg = t >> 3;
+  const int64_t b = blockIdx.x / P, r0 = (int64_t)(blockIdx.x % P) * QK_ROWS;
+  const int nblk = __builtin_amdgcn_readfirstlane((int)((rows - r0) / 256 < 4 ? (rows - r0) / 256 : 4));
+  const int ld4 = (int)(ldx * 4);
+  float4 v[16];
+  qk_load_chunk(X, ldx, r0, b, nblk, (4 * rg) * ld4 + slot * 16, ld4, v);
+  if (t < QK_COLS) s_inv[t] = recip_rn(scale[b * QK_COLS + t]);
+  __syncthreads();
+  const float i0 = s_inv[slot * 4], i1 = s_inv[slot * 4 + 1], i2 = s_inv[slot * 4 + 2], i3 = s_inv[slot * 4 + 3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned int w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 x = v[i * 4 + e];
+      w0 |= ((unsigned int)quantize1(x.x, i0) & 0xFFu) << (8 * e);
+      w1 |= ((unsigned int)quantize1(x.y, i1) & 0xFFu) << (8 * e);
+      w2 |= ((unsigned int)quantize1(x.z, i2) & 0xFFu) << (8 * e);
+      w3 |= ((unsigned int)quantize1(x.w, i3) & 0xFFu) << (8 * e);
+    }
+    tile[slot * 4 + 0][rg + 64 * i] = w0;
+    tile[slot * 4 + 1][rg + 64 * i] = w1;
+    tile[slot * 4 + 2][rg + 64 * i] = w2;
+    tile[slot * 4 + 3][rg + 64 * i] = w3;
+  }
+  __syncthreads();
+  const int jj = t >> 4, part = t & 15;                 // Qt row b*32+jj, bytes part*64 .. +64
+  int8_t* dst = Qt + (b * QK_COLS + jj) * ldqt + r0 + part * 64;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int w = part * 16 + qq * 4;
+    if (r0 + part * 64 + qq * 16 < rows)                 // rows % 256 == 0: whole 16-byte groups
+      *reinterpret_cast<uint4*>(dst + qq * 16) = make_uint4(tile[jj][w], tile[jj][w + 1], tile[jj][w + 2], tile[jj][w + 3]);
+  }
+}
+
 // Eligibility of the cooperative path for a column pass (see above).
 static bool qcols_coop_shape_ok(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Qt,
                                 int64_t ldqt, int fmt) {
@@ -546,8 +664,20 @@ static bool qcols_coop_shape_ok(const float* X, int64_t rows, int64_t cols, int6
 static bool qcols_takes_coop(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Qt,
                              int64_t ldqt, int fmt) {
   const int path = qcols_path_requested();
-  if (path == 1 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
+  if (path == 1 || path == 3 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
   return path == 2 || (double)rows * (double)cols * 4.0 >= kQkMinBytes;
+}
+
+// The two whole-line passes (qcols_lines_*), for tall and narrow inputs:
+// measured on MI355X (launch by launch / replayed from a graph), 8192x768
+// 11.6 / 12.1 us against 14.6 / 16.5 for the band kernel; 8192x2304 35.5
+// against 31.8 and 8192x3072 42.8 against 38.8, where the band kernel's
+// wider grid wins; 3072x768 10.2 against 6.5.
+static bool qcols_takes_lines(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Qt,
+                              int64_t ldqt, int fmt) {
+  const int path = qcols_path_requested();
+  if (path == 1 || path == 2 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
+  return path == 3 || (rows >= 4096 && cols <= 1024);
 }
 
 // Workgroups of qcols_coop_kernel<FMT> resident per CU on the current device
@@ -753,6 +883,16 @@ hipError_t quantize_cols_int8(const float* X, int64_t rows, int64_t cols, int64_
   if (qcols_takes_coop(X, rows, cols, ldx, Qt, ldqt, FMT)) {
     if (launch_qcols_coop<FMT>(X, rows, cols, ldx, Qt, ldqt, scale, stream) == hipSuccess) return hipSuccess;
     (void)hipGetLastError();   // the cooperative launch was refused: the paths below
+  }
+  if (qcols_takes_lines(X, rows, cols, ldx, Qt, ldqt, FMT)) {
+    const int P = (int)((rows + QK_ROWS - 1) / QK_ROWS);
+    const unsigned int grid = (unsigned int)(cols / QK_COLS * P);
+    hipLaunchKernelGGL(qcols_init_kernel<FMT>, dim3((unsigned int)((cols + 255) / 256)), dim3(256), 0, stream,
+                       scale, cols);
+    hipLaunchKernelGGL(qcols_lines_max_kernel<FMT>, dim3(grid), dim3(QK_THREADS), 0, stream, X, rows, ldx, scale, P);
+    hipLaunchKernelGGL(qcols_lines_quant_kernel, dim3(grid), dim3(QK_THREADS), 0, stream, X, rows, ldx, Qt, ldqt,
+                       scale, P);
+    return hipGetLastError();
   }
   int bc = rows > 0 ? qcols_band(rows, cols) : 0;
   // the test override can force the two-pass kernels (the bytes never
@@ -1000,7 +1140,12 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
   q.vec_out = ((uintptr_t)Q % 16 == 0) && (ldq % 16 == 0);
   const int bc = qcols_band(rows, cols);
   if (bc == 0 || qcols_path_requested() == 1) return false;   // the multi-kernel path
-  if (qcols_takes_coop(X, rows, cols, ldx, Q, ldq, fmt)) return false;   // a launch of its own
+  // the cooperative path needs a launch of its own; a pass the whole-line
+  // kernels would take alone stays a band job here, where it overlaps the
+  // batch's other passes (measured on a transformer layer's 24 input passes:
+  // 309 us batched against 337 with five 8192x768 column passes launched
+  // apart), unless a test forces the whole-line path
+  if (qcols_takes_coop(X, rows, cols, ldx, Q, ldq, fmt) || qcols_path_requested() == 3) return false;
   q.kind = QK_COLS_REG; q.param = bc;
   q.blocks = (int)((cols + bc - 1) / bc);
   return true;

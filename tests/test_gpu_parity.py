@@ -130,17 +130,18 @@ def test_quantize_cols_two_pass(g, rows, cols):
 COOP_SHAPES = [(1024, 32), (1280, 96), (3072, 768), (2048, 4096), (8192, 800), (4352, 6400)]
 
 
+@pytest.mark.parametrize("path", [2, 3])
 @pytest.mark.parametrize("rows,cols", COOP_SHAPES)
-def test_quantize_cols_cooperative(g, rows, cols):
-    """The cooperative column kernel (partial maxima exchanged between the
-    workgroups of a band, counter in the band's first Qt bytes), forced on
-    shapes below its size threshold, against the oracle; also with
-    power-of-two scales."""
-    say("quantize_cols cooperative", rows, cols)
+def test_quantize_cols_cooperative(g, rows, cols, path):
+    """The whole-line column kernels, forced on their shapes: the cooperative
+    one-read kernel (path 2: partial maxima exchanged between the workgroups
+    of a band, counter in the band's first Qt bytes) and the two whole-line
+    passes (path 3), against the oracle; also with power-of-two scales."""
+    say("quantize_cols whole-line path", path, rows, cols)
     X = np.ascontiguousarray(_quant_input(cols, rows, rows * 31 + cols).T)
     X[:, 3] = 0
     dX = to_dev(X)
-    with g.plan_overrides(qcols_path=2):
+    with g.plan_overrides(qcols_path=path):
         Qt, s = g.quantize_cols(dX)
         Qp, sp = g.quantize_cols_fmt(dX, g.FMT_POW2)
         torch.cuda.synchronize()
