@@ -282,8 +282,8 @@ size_t output_hash_workspace_bytes(void) { return kWsHeader + (size_t)kHashMaxPa
 
 size_t gemm_i8_requant_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0) return 256;
-  const GemmPlan plan = plan_gemm_requant(M, N, K > 0 ? K : 1);
-  return requant_rowmax_offset(plan) + (size_t)M * 4;
+  const GemmPlan plan = plan_gemm_requant(M, N, K > 0 ? K : 1, N);
+  return requant_layout(plan, M).bytes;
 }
 
 int gemm_i8_requant(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt, int64_t ldb,
@@ -313,9 +313,9 @@ int gemm_i8_requant(const int8_t* QA, int64_t lda, const float* s_row, const int
   if (K > 0 && (((uintptr_t)QA % 16) || ((uintptr_t)QBt % 16) || (lda % 16) || (ldb % 16) || lda < k16 ||
                 ldb < k16))
     return I8G_EALIGN;
-  const GemmPlan plan = plan_gemm_requant(M, N, K > 0 ? K : 1);
-  const size_t rm_off = requant_rowmax_offset(plan);
-  if (workspace_bytes < rm_off + (size_t)M * 4) return I8G_EWORKSPACE;
+  const GemmPlan plan = plan_gemm_requant(M, N, K > 0 ? K : 1, ldq);
+  const RequantLayout lay = requant_layout(plan, M);
+  if (workspace_bytes < lay.bytes) return I8G_EWORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   GemmParams p{};
   p.A = QA;
@@ -342,11 +342,13 @@ int gemm_i8_requant(const int8_t* QA, int64_t lda, const float* s_row, const int
   p.partials = nullptr;
   p.comb_rows = plan.comb_rows;
   p.hash_out = hash;
-  p.rowmax = reinterpret_cast<unsigned int*>(ws + rm_off);
+  p.rowmax = reinterpret_cast<unsigned int*>(ws + lay.max_offset);
+  p.inv_row = plan.persistent ? reinterpret_cast<const float*>(ws + lay.inv_offset) : nullptr;
+  p.qvec = (((uintptr_t)Q % 4) == 0 && ldq % 4 == 0 && N % 4 == 0) ? 1 : 0;
   p.Q = Q;
   p.ldq = ldq;
   p.s_out = s_out;
-  return hip_status(launch_gemm_requant(p, plan, st));
+  return hip_status(launch_gemm_requant(p, plan, lay, st));
 }
 
 int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const int8_t* QBt,

@@ -1198,7 +1198,7 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU, int STAGES, int WPC, bool NTSTORE>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool RELU, int STAGES, int WPC, bool NTSTORE, int MODE = 0>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WPC)
 gemm_i8_persist128_kernel(const GemmParams p) {
   constexpr int NWAVES = WAVES_M * WAVES_N, NT = NWAVES * 64;
@@ -1215,7 +1215,9 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   static_assert(A_INS * 8 * NWAVES == BM && B_INS * 8 * NWAVES == BN, "rows per stage");
   constexpr int LPS = A_INS + B_INS;                    // loads per wave per stage
   constexpr int RING = STAGES * STAGE;
-  constexpr int SCL = BM + BN;                          // floats per scale slot: rows, then columns
+  // floats per scale slot: row scales, column scales, and in MODE 2 the
+  // reciprocals of the output row scales
+  constexpr int SCL = BM + BN + (MODE == 2 ? BM : 0);
   constexpr int NSI = SCL / 64;                         // dword loads per scale slot
   static_assert(NSI * 64 == SCL, "tile sides are multiples of 64");
   constexpr int SQ = (NSI + NWAVES - 1) / NWAVES;
@@ -1253,7 +1255,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // ---- direct-to-LDS loads: lane l of a load fills row l/8, position l%8 ----
   const int r_in = lane >> 3, pch = lane & 7;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int wm_s = wave_s / WAVES_N;
+  const int wm_s = wave_s / WAVES_N, wn_s = wave_s % WAVES_N;
   // Loads go through buffer resources: the tile (and stage) base is scalar,
   // and each lane's offset is the same for every tile.  B rows at or beyond N
   // and column scales at or beyond N fall outside the resource's range and
@@ -1263,6 +1265,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     const int8_t* bbase;   // B at the tile's first row
     const float* rbase;    // s_row at the tile's first row
     const float* cbase;    // s_col at the tile's first column
+    const float* ibase;    // MODE 2: the output scale reciprocals at the tile's first row
     int ncol;              // columns of the tile inside the matrix
     int slot;              // scale slot of the tile
   };
@@ -1285,6 +1288,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     s.bbase = uniform_ptr(p.B + (int64_t)col0 * p.ldb);
     s.rbase = uniform_ptr(p.s_row + row0);
     s.cbase = uniform_ptr(p.s_col + col0);
+    if constexpr (MODE == 2) s.ibase = uniform_ptr(p.inv_row + row0);
     s.ncol = __builtin_amdgcn_readfirstlane(N - col0 < BN ? N - col0 : BN);
   };
   // The loads of one stage: LPS per wave, A's row blocks first, then B's.
@@ -1313,8 +1317,9 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   auto issue_ops = [&](int buf, const Src& s, int kt) __attribute__((always_inline)) {
     dma_range(dma_setup(buf, s, kt), std::integral_constant<int, 0>(), std::integral_constant<int, LPS>());
   };
-  // the tile's row and column scales into slot s.slot: load k (k = q*4 + wave)
-  // covers entries 64k .. 64k+63 of [rows | columns]
+  // the tile's row and column scales (and in MODE 2 the output scale
+  // reciprocals) into slot s.slot: load k (k = q*4 + wave) covers entries
+  // 64k .. 64k+63 of [rows | columns | reciprocals]
   auto issue_scales = [&](const Src& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < SQ; ++q) {
@@ -1323,6 +1328,9 @@ gemm_i8_persist128_kernel(const GemmParams p) {
         __amdgpu_buffer_rsrc_t rs;
         if (k * 64 < BM) {
           rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s.rbase + k * 64), 0, 256, 0x00020000);
+        } else if (MODE == 2 && k * 64 >= BM + BN) {
+          rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s.ibase + (k * 64 - BM - BN)), 0, 256,
+                                                 0x00020000);
         } else {
           const int c0 = k * 64 - BM;
           const int left = s.ncol - c0;
@@ -1355,9 +1363,13 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   struct Out {
     float* cbase;          // C at the tile's first row
     int voff[FN];          // this lane's column byte offset (+4 rows for lanes 32..63), or kBufInvalid
+    int voffq[FN];         // MODE 2 packed codes: row 4*(lane/32) + lane%4, columns from 4*((lane%32)/4)
     uint32_t sr_base;      // LDS address of this lane's first row scale of the wave's rows
     uint32_t rk_base;      // LDS address of this lane's first row key of the wave's rows
     uint32_t sc_base;      // LDS address of this lane's column scale in the wave's first block column
+    uint32_t iv_base;      // MODE 2: LDS address of this lane's first output scale reciprocal
+    int8_t* qbase;         // MODE 2: the codes at the tile's first row
+    unsigned int* pbase;   // MODE 1: this wave's row maxima of the tile (partial p = tn * WAVES_N + wn)
     int col0;              // the tile's first column
     int slot;              // scale / key slot of the tile
   };
@@ -1365,13 +1377,24 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   uint64_t lane_hash = 0;  // this lane's share of S over every drained tile
   auto make_out = [&](int r, int tm, int tn, Out& o) __attribute__((always_inline)) {
     const int row0 = tm * BM;
-    o.cbase = uniform_ptr(p.C + (int64_t)row0 * p.ldc);
     o.slot = __builtin_amdgcn_readfirstlane(r % 3);
+    if constexpr (MODE == 0) o.cbase = uniform_ptr(p.C + (int64_t)row0 * p.ldc);
+    if constexpr (MODE == 1)
+      o.pbase = uniform_ptr(p.rowmax + (int64_t)(tn * WAVES_N + wn_s) * M + row0 + wm_s * WTM);
+    if constexpr (MODE == 2) {
+      o.qbase = uniform_ptr(p.Q + (int64_t)row0 * p.ldq);
+      o.iv_base = lds_addr(s_scl + o.slot * SCL + BM + BN) + (wm * WTM + lhalf * 4) * 4;
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = tn * BN + wn * WTN + j * 32 + lrow;
       const bool ok = col < N;
-      o.voff[j] = ok ? (int)(lhalf * 4 * ldc4 + col * 4) : kBufInvalid;
+      if constexpr (MODE == 2) {
+        o.voff[j] = ok ? (int)(lhalf * 4 * p.ldq + col) : kBufInvalid;
+        const int col4 = col & ~3;
+        o.voffq[j] = col4 < N ? (int)((lhalf * 4 + (lrow & 3)) * p.ldq + col4) : kBufInvalid;
+      } else
+        o.voff[j] = ok ? (int)(lhalf * 4 * ldc4 + col * 4) : kBufInvalid;
     }
     o.col0 = tn * BN;
     o.sr_base = lds_addr(s_scl + o.slot * SCL) + (wm * WTM + lhalf * 4) * 4;
@@ -1387,6 +1410,17 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   struct DHalf {
     v4i sr[2];
     v4i rk[2];
+    v4i iv[2];   // MODE 2: the output scale reciprocals of the same rows
+  };
+  // MODE 2: the reciprocals of a half, at the same offset as its row scales
+  auto read_iv = [&](const Out& o, auto OFF, DHalf& d) __attribute__((always_inline)) {
+    constexpr int off = decltype(OFF)::value;
+    asm volatile(
+        "ds_read_b128 %[i0], %[iv] offset:%[o0]\n\t"
+        "ds_read_b128 %[i1], %[iv] offset:%[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [i0] "=&v"(d.iv[0]), [i1] "=&v"(d.iv[1])
+        : [iv] "v"(o.iv_base), [o0] "i"(off), [o1] "i"(off + 32));
   };
   // Byte offsets (immediates of the LDS reads): the row scales / keys of half
   // h of block row i start 32i + 16h rows into the wave's rows; the column
@@ -1412,6 +1446,10 @@ gemm_i8_persist128_kernel(const GemmParams p) {
         : [sr1] "v"(o1.sr_base), [rk1] "v"(o1.rk_base), [sr2] "v"(o2.sr_base),
           [rk2] "v"(o2.rk_base), [sc2] "v"(o2.sc_base), [ol0] "i"(ol), [ol1] "i"(ol + 32),
           [oe0] "i"(oe), [oe1] "i"(oe + 32), [oc] "i"(oc));
+    if constexpr (MODE == 2) {
+      read_iv(o1, std::integral_constant<int, ol>(), late);
+      read_iv(o2, std::integral_constant<int, oe>(), early);
+    }
   };
   // the second half of block b of o
   auto read_late = [&](const Out& o, auto B, DHalf& late) __attribute__((always_inline)) {
@@ -1426,6 +1464,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
         : [l0] "=&v"(late.sr[0]), [l1] "=&v"(late.sr[1]), [l2] "=&v"(late.rk[0]),
           [l3] "=&v"(late.rk[1])
         : [sr] "v"(o.sr_base), [rk] "v"(o.rk_base), [o0] "i"(ol), [o1] "i"(ol + 32));
+    if constexpr (MODE == 2) read_iv(o, std::integral_constant<int, ol>(), late);
   };
   // the first half and column scale of block c of o
   auto read_early = [&](const Out& o, auto C, DHalf& early, int& sc) __attribute__((always_inline)) {
@@ -1442,6 +1481,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
           [e3] "=&v"(early.rk[1]), [sc] "=&v"(sc)
         : [sr] "v"(o.sr_base), [rk] "v"(o.rk_base), [sca] "v"(o.sc_base), [o0] "i"(oe),
           [o1] "i"(oe + 32), [oc] "i"(oc));
+    if constexpr (MODE == 2) read_iv(o, std::integral_constant<int, oe>(), early);
   };
   // Element 4q+e of block b = (i, j) of accumulator set Y: lane l holds
   // column l % 32 and row 8q + 4*(l/32) + e of the block.
@@ -1450,7 +1490,13 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // and the MFMAs: step 0 converts the accumulators, 1 applies the row
   // scales, 2 the column scale (and ReLU), 3 adds the hash terms of elements
   // 0-1 and stores them, 4 the same for elements 2-3.
+  unsigned int rmx[FM][16];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rmx[i][v] = 0u;
   float xq[4];
+  int qc[4];   // MODE 2: the codes of the part being drained
   auto drain_step = [&](v16i (&Y)[FM][FN], const Out& o, const DHalf& d, int scb, auto IJ, auto Q,
                         auto STEP) __attribute__((always_inline)) {
     constexpr int b = decltype(IJ)::value, q = decltype(Q)::value, st = decltype(STEP)::value;
@@ -1467,6 +1513,39 @@ gemm_i8_persist128_kernel(const GemmParams p) {
         xq[e] = mul_rn(xq[e], __int_as_float(scb));
         if (RELU) xq[e] = relu_pos0(xq[e]);
       }
+    } else if constexpr (MODE == 1) {
+      constexpr int e0 = (st - 3) * 2;
+#pragma unroll
+      for (int e = e0; e < e0 + 2; ++e) {
+        const unsigned int a = __float_as_uint(xq[e]) & 0x7FFFFFFFu;
+        rmx[i][q * 4 + e] = a > rmx[i][q * 4 + e] ? a : rmx[i][q * 4 + e];
+      }
+    } else if constexpr (MODE == 2) {
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(o.qbase + (int64_t)(wm_s * WTM + i * 32) * p.ldq), 0, (int)kBufRecords, 0x00020000);
+      constexpr int e0 = (st - 3) * 2;
+#pragma unroll
+      for (int e = e0; e < e0 + 2; ++e) {
+        tcol[j] += (uint64_t)(unsigned int)d.rk[q % 2][e] * (uint64_t)__float_as_uint(xq[e]);
+        qc[e] = quantize1(xq[e], __int_as_float(d.iv[q % 2][e]));
+        if (!p.qvec)
+          __builtin_amdgcn_raw_buffer_store_b8((unsigned char)qc[e], rsrc, o.voff[j], (q * 8 + e) * (int)p.ldq, 0);
+      }
+      if constexpr (st == 4) {
+        asm volatile("" : "+v"(tcol[j]));
+        if (p.qvec) {
+          // the four codes of this lane (rows 0-3 of the part, one column)
+          // become four columns of one row: a 4x4 byte transpose inside
+          // each quad of lanes (the quad's lanes hold four adjacent columns)
+          const unsigned int w = ((unsigned int)qc[0] & 0xFFu) | (((unsigned int)qc[1] & 0xFFu) << 8) |
+                                 (((unsigned int)qc[2] & 0xFFu) << 16) | ((unsigned int)qc[3] << 24);
+          const unsigned int x = (unsigned int)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);
+          const unsigned int a = __builtin_amdgcn_perm(x, w, (lrow & 2) ? 0x03020706u : 0x05040100u);
+          const unsigned int y = (unsigned int)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
+          const unsigned int t = __builtin_amdgcn_perm(y, a, (lrow & 1) ? 0x03070105u : 0x06020400u);
+          __builtin_amdgcn_raw_buffer_store_b32(t, rsrc, o.voffq[j], q * 8 * (int)p.ldq, 0);
+        }
+      }
     } else {
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(o.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
@@ -1479,6 +1558,59 @@ gemm_i8_persist128_kernel(const GemmParams p) {
                                               NTSTORE ? kStoreNT : 0);
       }
       if constexpr (st == 4) asm volatile("" : "+v"(tcol[j]));
+    }
+  };
+  // MODE 1: the maxima of |y| of the tile being drained, over this lane's
+  // column, per element row of each block row: rows 8q + 4*(lane/32) + e of
+  // block row i in rmx[i][4q + e].  close_tile_max reduces them over the 32
+  // lanes of each half-wave (four halving exchanges, then a last one between
+  // lane pairs, after which lanes 2v and 2v+1 hold the maximum of element
+  // row v) and stores one word per row: the wave's partial maximum of that
+  // row over its WTN columns of the tile.
+  auto close_tile_max = [&](const Out& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      unsigned int x8[8], x4[4], x2[2];
+      const bool b4 = (lrow & 16) != 0, b3 = (lrow & 8) != 0, b2 = (lrow & 4) != 0, b1 = (lrow & 2) != 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const unsigned int keep = b4 ? rmx[i][8 + k] : rmx[i][k];
+        const unsigned int give = b4 ? rmx[i][k] : rmx[i][8 + k];
+        const unsigned int got = (unsigned int)__shfl_xor((int)give, 16, 64);
+        x8[k] = got > keep ? got : keep;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const unsigned int keep = b3 ? x8[4 + k] : x8[k];
+        const unsigned int give = b3 ? x8[k] : x8[4 + k];
+        const unsigned int got = (unsigned int)__shfl_xor((int)give, 8, 64);
+        x4[k] = got > keep ? got : keep;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const unsigned int keep = b2 ? x4[2 + k] : x4[k];
+        const unsigned int give = b2 ? x4[k] : x4[2 + k];
+        const unsigned int got = (unsigned int)__shfl_xor((int)give, 4, 64);
+        x2[k] = got > keep ? got : keep;
+      }
+      unsigned int m;
+      {
+        const unsigned int keep = b1 ? x2[1] : x2[0];
+        const unsigned int give = b1 ? x2[0] : x2[1];
+        const unsigned int got = (unsigned int)__shfl_xor((int)give, 2, 64);
+        m = got > keep ? got : keep;
+      }
+      const unsigned int other = (unsigned int)__shfl_xor((int)m, 1, 64);
+      m = other > m ? other : m;
+      // element row v = 8*b4 + 4*b3 + 2*b2 + b1 of this half: block row
+      // 8*(v/4) + 4*(lane/32) + v%4
+      const int v = (lrow >> 1) & 15;
+      const int row = i * 32 + 8 * (v >> 2) + 4 * lhalf + (v & 3);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(o.pbase, 0, (int)kBufRecords, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b32(m, rs, (lrow & 1) == 0 ? row * 4 : kBufInvalid, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) rmx[i][k] = 0u;
     }
   };
   auto close_tile_hash = [&](const Out& o) __attribute__((always_inline)) {
@@ -1601,16 +1733,21 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   Out out_cur, out_prev;
   // a workgroup without tiles stores nothing: every offset lies outside the range
   out_cur.cbase = p.C;
+  out_cur.qbase = p.Q;
+  out_cur.pbase = p.rowmax;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) out_cur.voff[j] = kBufInvalid;
-  out_cur.sr_base = out_cur.rk_base = out_cur.sc_base = 0;
+  for (int j = 0; j < FN; ++j) out_cur.voff[j] = out_cur.voffq[j] = kBufInvalid;
+  out_cur.sr_base = out_cur.rk_base = out_cur.sc_base = out_cur.iv_base = 0;
   out_cur.col0 = 0;
   out_cur.slot = 0;
   // Stores of the previous stage issued after the loads a stage waits for:
   // all sixteen with three or more slots (those loads were issued a stage
   // earlier), with two slots only the four of its k-step 3 (the loads share
-  // that k-step and precede its stores).
-  constexpr int PREV_ST = STAGES >= 3 ? 16 : 4;
+  // that k-step and precede its stores).  MODE 1 drains without stores.
+  // MODE 1 drains without stores; MODE 2 stores at least one word per part
+  // (four per stage when its codes are packed, sixteen bytes otherwise).
+  constexpr int PREV_ST = MODE == 1 ? 0 : MODE == 2 ? (STAGES >= 3 ? 4 : 1) : (STAGES >= 3 ? 16 : 4);
+  constexpr int CUR_ST = MODE == 1 ? 0 : MODE == 2 ? 3 : 12;   // stores of k-steps 0-2 of a draining stage
   auto run_tile = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int r, auto DRAIN)
       __attribute__((always_inline)) {
     constexpr bool D = decltype(DRAIN)::value;
@@ -1618,7 +1755,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     const bool has_next = r + 1 < my_tiles;
     static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
       constexpr int b = decltype(BI)::value;
-      constexpr int ST = (STAGES - 2) * LPS + (D && b >= 1 ? PREV_ST : 0) + (D ? 12 : 0);
+      constexpr int ST = (STAGES - 2) * LPS + (D && b >= 1 ? PREV_ST : 0) + (D ? CUR_ST : 0);
       DHalf& ec = (b % 2 == 0) ? e0 : e1;
       DHalf& en = (b % 2 == 0) ? e1 : e0;
       int& sc_c = (b % 2 == 0) ? s0 : s1;
@@ -1640,7 +1777,12 @@ gemm_i8_persist128_kernel(const GemmParams p) {
       stage(X, Y, g0 + b, out_prev, ec, sc_c, late, std::integral_constant<bool, b == 0>(), DRAIN, BI,
             std::integral_constant<int, ST>(), mid);
     });
-    if (D) close_tile_hash(out_prev);
+    if (D) {
+      if constexpr (MODE == 1)
+        close_tile_max(out_prev);
+      else
+        close_tile_hash(out_prev);
+    }
     static_assert(NB % 2 == 0, "stage NB (if any) finds its next early half in e0");
     for (int s = NB; s < nst; ++s) {
       auto mid = [&]() __attribute__((always_inline)) {
@@ -1690,7 +1832,23 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     // and vmcnt retires in order) does not wait behind the tile's stores.
     // Every direct-to-LDS load has landed here, so plain LDS reads are used.
     wait_vmcnt<0>();
-    if (p.do_hash) {
+    if constexpr (MODE == 1) {
+      static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
+        constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
+        const int r0 = wm * WTM + i * 32 + lhalf * 4;
+        const float* srp = s_scl + out_cur.slot * SCL + r0;
+        const float sc = s_scl[out_cur.slot * SCL + BM + wn * WTN + j * 32 + lrow];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = (v >> 2) * 8 + (v & 3);
+          float y = epilogue1(acc0[i][j][v], srp[rr], sc);
+          if (RELU) y = relu_pos0(y);
+          const unsigned int a = __float_as_uint(y) & 0x7FFFFFFFu;
+          rmx[i][v] = a > rmx[i][v] ? a : rmx[i][v];
+        }
+      });
+      close_tile_max(out_cur);
+    } else if (p.do_hash) {
       static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
         constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
         const int r0 = wm * WTM + i * 32 + lhalf * 4;
@@ -1715,12 +1873,42 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // waiting until at most those stores are outstanding means the share is
   // acknowledged), takes its ticket, and issues the second half before it
   // needs the ticket's value.
+  // pass 1 of the requantizing epilogue ends here: no output, no hash
+  if constexpr (MODE == 1) return;
   constexpr int HALF = NB / 2;
   auto store_block = [&](auto BI) __attribute__((always_inline)) {
     constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
     const int r0 = wm * WTM + i * 32 + lhalf * 4;
     const float* srp = s_scl + out_cur.slot * SCL + r0;
     const float sc = s_scl[out_cur.slot * SCL + BM + wn * WTN + j * 32 + lrow];
+    if constexpr (MODE == 2) {
+      const float* ivp = s_scl + out_cur.slot * SCL + BM + BN + r0;
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(out_cur.qbase + (int64_t)(wm_s * WTM + i * 32) * p.ldq), 0, (int)kBufRecords, 0x00020000);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int c4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = q * 8 + e;
+          float y = epilogue1(acc0[i][j][q * 4 + e], srp[rr], sc);
+          if (RELU) y = relu_pos0(y);
+          c4[e] = quantize1(y, ivp[rr]);
+          if (!p.qvec)
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)c4[e], rq, out_cur.voff[j], rr * (int)p.ldq, 0);
+        }
+        if (p.qvec) {   // the quad transpose of the drain
+          const unsigned int w = ((unsigned int)c4[0] & 0xFFu) | (((unsigned int)c4[1] & 0xFFu) << 8) |
+                                 (((unsigned int)c4[2] & 0xFFu) << 16) | ((unsigned int)c4[3] << 24);
+          const unsigned int x = (unsigned int)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);
+          const unsigned int a = __builtin_amdgcn_perm(x, w, (lrow & 2) ? 0x03020706u : 0x05040100u);
+          const unsigned int y = (unsigned int)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
+          const unsigned int t = __builtin_amdgcn_perm(y, a, (lrow & 1) ? 0x03070105u : 0x06020400u);
+          __builtin_amdgcn_raw_buffer_store_b32(t, rq, out_cur.voffq[j], q * 8 * (int)p.ldq, 0);
+        }
+      }
+      return;
+    }
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(out_cur.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
         0x00020000);
@@ -2100,22 +2288,77 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
 
 
 // ---------------------------------------------------------------------------
-// requantizing epilogue: zero the row maxima, pass 1 (row maxima), pass 2
-// (codes, scales, hash).  Both passes run the same tile walk and the same
-// exact contraction, so pass 2 sees exactly the y that pass 1 reduced.
+// requantizing epilogue: pass 1 (row maxima of |y|), the row scales, pass 2
+// (codes, hash).  Both passes run the same tile walk and the same exact
+// contraction, so pass 2 sees exactly the y that pass 1 reduced.
+//  * Persistent (the 128x192 tile with 128-byte stages, where the shape
+//    allows it): pass 1 stores each wave's partial maximum of every row of
+//    its tile (no atomics: [tiles_n * 2][M] words), requant_scales_kernel
+//    reduces them to the row scales and their reciprocals, and pass 2 loads
+//    the reciprocals into the tile's scale slot beside the row and column
+//    scales.
+//  * Otherwise (the non-persistent tiles): the row maxima are zeroed, pass 1
+//    raises them with integer atomicMax, pass 2 turns them into scales.
 // ---------------------------------------------------------------------------
 __global__ void fill_zero_u32_kernel(unsigned int* p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
-GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K) {
+// s = max(RN(a/127), RN(1e-8)) of the largest partial maximum of row i, and
+// its reciprocal RN(1/s) -- the scale and reciprocal quantize_rows would
+// compute for row i of y.  A workgroup takes 64 rows; its four waves read
+// every fourth partial (coalesced along the rows) and meet in LDS.
+__global__ void __launch_bounds__(256) requant_scales_kernel(const unsigned int* part, int P, int M,
+                                                             float* s_out, float* inv) {
+  __shared__ unsigned int red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
+  unsigned int m = 0;
+  if (i < M) {
+#pragma unroll 4
+    for (int k = wave; k < P; k += 4) {
+      const unsigned int v = part[(int64_t)k * M + i];
+      m = v > m ? v : m;
+    }
+  }
+  red[wave][lane] = m;
+  __syncthreads();
+  if (wave == 0 && i < M) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) m = red[w][lane] > m ? red[w][lane] : m;
+    const float sc = scale_of_absmax(__uint_as_float(m));
+    s_out[i] = sc;
+    inv[i] = recip_rn(sc);
+  }
+}
+
+constexpr int kRequantPersistCfg = 6;
+
+GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K, int64_t ldq) {
   int force = g_force_tile.load(std::memory_order_relaxed);
+  if ((force < 0 || force == kRequantPersistCfg) && ldq <= (int64_t(1) << 24)) {
+    const GemmPlan pp = plan_gemm_forced(M, N, K, true, kRequantPersistCfg, 1);
+    if (pp.cfg == kRequantPersistCfg) return pp;
+  }
   if (force > 2) force = -1;
   return plan_gemm_forced(M, N, K, false, force, 1);
 }
 
-size_t requant_rowmax_offset(const GemmPlan& plan) { return (plan.workspace_bytes + 255) / 256 * 256; }
+RequantLayout requant_layout(const GemmPlan& plan, int64_t M) {
+  RequantLayout l;
+  l.max_offset = (plan.workspace_bytes + 255) / 256 * 256;
+  if (plan.persistent) {
+    l.partials = plan.tiles_n * 2;
+    l.inv_offset = l.max_offset + ((size_t)l.partials * M * 4 + 255) / 256 * 256;
+    l.bytes = l.inv_offset + (size_t)M * 4;
+  } else {
+    l.partials = 0;
+    l.inv_offset = 0;
+    l.bytes = l.max_offset + (size_t)M * 4;
+  }
+  return l;
+}
 
 template <int MODE>
 static void launch_dma_mode(const GemmParams& p, int cfg, unsigned int grid, hipStream_t stream) {
@@ -2132,10 +2375,29 @@ static void launch_dma_mode(const GemmParams& p, int cfg, unsigned int grid, hip
   }
 }
 
-hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, hipStream_t stream) {
+template <int MODE, int BM, int BN, int STAGES, int WPC>
+static void launch_persist_mode(const GemmParams& p, unsigned int grid, hipStream_t stream) {
+  if (p.relu)
+    hipLaunchKernelGGL((gemm_i8_persist128_kernel<BM, BN, 2, 2, true, STAGES, WPC, false, MODE>), dim3(grid),
+                       dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_i8_persist128_kernel<BM, BN, 2, 2, false, STAGES, WPC, false, MODE>), dim3(grid),
+                       dim3(256), 0, stream, p);
+}
+
+hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, const RequantLayout& l, hipStream_t stream) {
+  const int do_hash = p.do_hash;
+  if (plan.persistent) {
+    p.do_hash = 0;
+    launch_persist_mode<1, 128, 192, 3, 1>(p, (unsigned int)plan.grid, stream);
+    hipLaunchKernelGGL(requant_scales_kernel, dim3((unsigned int)((p.M + 63) / 64)), dim3(256), 0, stream,
+                       p.rowmax, l.partials, p.M, p.s_out, const_cast<float*>(p.inv_row));
+    p.do_hash = do_hash;
+    launch_persist_mode<2, 128, 192, 3, 1>(p, (unsigned int)plan.grid, stream);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned int)((p.M + 255) / 256)), dim3(256), 0, stream,
                      p.rowmax, p.M);
-  const int do_hash = p.do_hash;
   p.do_hash = 0;
   launch_dma_mode<1>(p, plan.cfg, (unsigned int)plan.grid, stream);
   p.do_hash = do_hash;

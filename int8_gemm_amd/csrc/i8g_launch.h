@@ -25,10 +25,13 @@ struct GemmParams {
   int comb_rows;                    // rows per split-K combine workgroup
   uint64_t* hash_out;
   int a4, b4;                       // operand stored as int4, two per byte (gemm_i4_kernel only)
-  // requantizing epilogue (gemm_i8_requant): pass 1 only raises rowmax[i]
-  // to the largest |y| bit pattern of row i; pass 2 writes the int8 codes of
-  // y with the row scales those maxima give
-  unsigned int* rowmax;             // M words, zero before pass 1
+  // requantizing epilogue (gemm_i8_requant): pass 1 only reduces |y| to row
+  // maxima (bit patterns); pass 2 writes the int8 codes of y with the row
+  // scales those maxima give
+  unsigned int* rowmax;             // non-persistent: M words, zero before pass 1;
+                                    // persistent: [tiles_n * 2][M] partial maxima
+  const float* inv_row;             // persistent pass 2: RN(1/s) of every output row scale s
+  int qvec;                         // persistent pass 2: Q, ldq and N multiples of 4 (codes stored 4 per lane)
   int8_t* Q;                        // pass 2: codes, row-major, leading dimension ldq
   int64_t ldq;
   float* s_out;                     // pass 2: the M row scales of the codes
@@ -100,9 +103,18 @@ void set_test_overrides(int force_tile, int force_splits, int qcols_path, int in
 int qcols_path_requested();
 // Requantizing epilogue: one K split, a non-persistent tile (a forced tile
 // 0..2 honoured for tests); the workspace adds M words of row maxima.
-GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K);
-size_t requant_rowmax_offset(const GemmPlan& plan);
-hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, hipStream_t stream);
+// The requantizing epilogue's plan: the persistent 128x192 tile where the
+// shape allows it (K % 128 == 0, K >= 768, M % 128 == 0, ldq <= 2^24), else
+// a non-persistent tile.  Its workspace after the GEMM's own: the row maxima
+// (non-persistent: M words; persistent: `partials` x M words, then the M
+// reciprocals at inv_offset).
+GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K, int64_t ldq);
+struct RequantLayout {
+  size_t max_offset, inv_offset, bytes;
+  int partials;
+};
+RequantLayout requant_layout(const GemmPlan& plan, int64_t M);
+hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, const RequantLayout& l, hipStream_t stream);
 
 // fmt: FMT_POW2 / FMT_INT4 bits (i8g_device.h); int4 outputs take
 // 16*ceil(len/32) bytes per line, 16-byte aligned.

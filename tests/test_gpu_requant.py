@@ -67,6 +67,69 @@ def test_requant_every_tile(g, tile):
     assert g.hash_value(h) == hashref.output_hash(Cw)
 
 
+# shapes the persistent 128x192 passes take (K % 128 == 0, K >= 768, M % 128
+# == 0): ragged last column tile, N below one tile, more tiles than
+# workgroups (the drained epilogue of the previous tile carries the row
+# maxima and the codes), a long K
+PERSIST_SHAPES = [(256, 200, 768, False), (512, 50, 1536, True), (4096, 1600, 768, True),
+                  (1280, 1000, 896, False), (384, 640, 3072, True)]
+
+
+@pytest.mark.parametrize("M,N,K,relu", PERSIST_SHAPES)
+def test_requant_persistent(g, M, N, K, relu):
+    """The persistent passes (partial row maxima per wave and tile, the
+    scale kernel, codes from the reciprocals in the scale slot) against the
+    oracle, with the hash of the never-stored f32 output."""
+    say("requant persistent", M, N, K, relu)
+    (QA, sA, QB, sB), dev = _operands(g, M, N, K, M * 3 + N + K)
+    Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, relu)
+    lib = g.load()
+    with g.plan_overrides(force_tile=6):
+        # the persistent plan's workspace holds a partial maximum per row for
+        # each wave column of each tile column (two per 192 columns)
+        assert lib.gemm_i8_requant_workspace_bytes(M, N, K) >= M * 4 * 2 * -(-N // 192)
+        Q, s, h = g.gemm_i8_requant(*dev, relu=relu, want_hash=True)
+        torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(Q.cpu().numpy(), Qw)
+    assert g.hash_value(h) == hashref.output_hash(Cw)
+    # the non-persistent passes give the same bytes
+    with g.plan_overrides(force_tile=2):
+        Q2, s2, h2 = g.gemm_i8_requant(*dev, relu=relu, want_hash=True)
+        torch.cuda.synchronize()
+    assert torch.equal(Q, Q2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
+    assert g.hash_value(h) == g.hash_value(h2)
+
+
+@pytest.mark.parametrize("pad", [52, 53])
+def test_requant_persistent_padded_ldq(g, pad):
+    """Codes written with a leading dimension larger than N: the padding
+    bytes between rows are left as they were (pad 52: codes stored four per
+    lane; pad 53, an odd leading dimension: one byte per lane)."""
+    M, N, K = 512, 300, 768
+    say("requant persistent ldq", M, N, K, pad)
+    (QA, sA, QB, sB), (dQA, dsA, dQB, dsB) = _operands(g, M, N, K, 515)
+    Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, True)
+    lib = g.load()
+    ldq = N + pad
+    Qp = torch.full((M, ldq), 77, dtype=torch.int8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    h = torch.zeros(1, dtype=torch.int64, device="cuda")
+    wsb = int(lib.gemm_i8_requant_workspace_bytes(M, N, K))
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib.gemm_i8_requant(dQA.data_ptr(), dQA.stride(0), dsA.data_ptr(), dQB.data_ptr(), dQB.stride(0),
+                             dsB.data_ptr(), M, N, K, Qp.data_ptr(), ldq, s.data_ptr(), 3, h.data_ptr(),
+                             ws.data_ptr(), wsb, st)
+    torch.cuda.synchronize()
+    assert rc == 0
+    Qh = Qp.cpu().numpy()
+    assert np.array_equal(Qh[:, :N], Qw)
+    assert np.all(Qh[:, N:] == 77)
+    assert np.array_equal(s.cpu().numpy(), sw)
+    assert g.hash_value(h) == hashref.output_hash(Cw)
+
+
 def test_requant_mlp_up_full_size(g):
     """GPT-2-small MLP up-projection 8192x3072x768 with ReLU: the codes and
     scales equal quantize_rows of the library's own f32 output and the
