@@ -235,6 +235,32 @@ def test_tile_and_split_invariance(g, tile):
         assert got["hash"] == h
 
 
+@pytest.mark.parametrize("N", [517, 518, 519])
+def test_split_reduction_ragged_columns(g, N):
+    """Split K with a column count that is not a multiple of 4 (the combine
+    reads and writes the last column group one word at a time), on three
+    tile configurations, and a second call with another shape on the same
+    workspace after each."""
+    rng = np.random.default_rng(N)
+    A = rng.standard_t(3, (700, 2048)).astype(F32)
+    B = rng.standard_normal((2048, N)).astype(F32)
+    C, *_ = ref.blockscaled_gemm(A, B, False)
+    h = hashref.output_hash(C)
+    A2 = rng.standard_t(3, (2304, 1024)).astype(F32)
+    B2 = rng.standard_normal((1024, 3000)).astype(F32)
+    C2, *_ = ref.blockscaled_gemm(A2, B2, True)
+    for tile, splits in ((2, 3), (1, 4), (0, 2)):
+        with g.plan_overrides(force_tile=tile, force_splits=splits):
+            assert g.plan_query(700, N, 2048) == (tile, splits)
+            say("split ragged N", N, "tile", tile, "splits", splits)
+            got = run_method(g, A, B, relu=False)
+            assert_bits(got["C"], C, f"C N {N} tile {tile} splits {splits}")
+            assert got["hash"] == h
+            got2 = run_method(g, A2, B2, relu=True)
+            assert_bits(got2["C"], C2, f"C2 tile {tile} splits {splits}")
+            assert got2["hash"] == hashref.output_hash(C2)
+
+
 # (M, N, K, relu): ragged edges; more tiles than CUs so that workgroups walk
 # several tiles (and some one fewer); K with fewer 64-byte stages than a
 # wave has output blocks, and with more
