@@ -344,7 +344,6 @@ int gemm_i8_requant(const int8_t* QA, int64_t lda, const float* s_row, const int
   p.hash_out = hash;
   p.rowmax = reinterpret_cast<unsigned int*>(ws + lay.max_offset);
   p.inv_row = plan.persistent ? reinterpret_cast<const float*>(ws + lay.inv_offset) : nullptr;
-  p.qvec = (((uintptr_t)Q % 4) == 0 && ldq % 4 == 0 && N % 4 == 0) ? 1 : 0;
   p.Q = Q;
   p.ldq = ldq;
   p.s_out = s_out;

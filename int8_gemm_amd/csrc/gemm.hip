@@ -1363,7 +1363,6 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   struct Out {
     float* cbase;          // C at the tile's first row
     int voff[FN];          // this lane's column byte offset (+4 rows for lanes 32..63), or kBufInvalid
-    int voffq[FN];         // MODE 2 packed codes: row 4*(lane/32) + lane%4, columns from 4*((lane%32)/4)
     uint32_t sr_base;      // LDS address of this lane's first row scale of the wave's rows
     uint32_t rk_base;      // LDS address of this lane's first row key of the wave's rows
     uint32_t sc_base;      // LDS address of this lane's column scale in the wave's first block column
@@ -1389,11 +1388,9 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     for (int j = 0; j < FN; ++j) {
       const int col = tn * BN + wn * WTN + j * 32 + lrow;
       const bool ok = col < N;
-      if constexpr (MODE == 2) {
+      if constexpr (MODE == 2)
         o.voff[j] = ok ? (int)(lhalf * 4 * p.ldq + col) : kBufInvalid;
-        const int col4 = col & ~3;
-        o.voffq[j] = col4 < N ? (int)((lhalf * 4 + (lrow & 3)) * p.ldq + col4) : kBufInvalid;
-      } else
+      else
         o.voff[j] = ok ? (int)(lhalf * 4 * ldc4 + col * 4) : kBufInvalid;
     }
     o.col0 = tn * BN;
@@ -1496,7 +1493,6 @@ gemm_i8_persist128_kernel(const GemmParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) rmx[i][v] = 0u;
   float xq[4];
-  int qc[4];   // MODE 2: the codes of the part being drained
   auto drain_step = [&](v16i (&Y)[FM][FN], const Out& o, const DHalf& d, int scb, auto IJ, auto Q,
                         auto STEP) __attribute__((always_inline)) {
     constexpr int b = decltype(IJ)::value, q = decltype(Q)::value, st = decltype(STEP)::value;
@@ -1527,25 +1523,10 @@ gemm_i8_persist128_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = e0; e < e0 + 2; ++e) {
         tcol[j] += (uint64_t)(unsigned int)d.rk[q % 2][e] * (uint64_t)__float_as_uint(xq[e]);
-        qc[e] = quantize1(xq[e], __int_as_float(d.iv[q % 2][e]));
-        if (!p.qvec)
-          __builtin_amdgcn_raw_buffer_store_b8((unsigned char)qc[e], rsrc, o.voff[j], (q * 8 + e) * (int)p.ldq, 0);
+        const int qv = quantize1(xq[e], __int_as_float(d.iv[q % 2][e]));
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)qv, rsrc, o.voff[j], (q * 8 + e) * (int)p.ldq, 0);
       }
-      if constexpr (st == 4) {
-        asm volatile("" : "+v"(tcol[j]));
-        if (p.qvec) {
-          // the four codes of this lane (rows 0-3 of the part, one column)
-          // become four columns of one row: a 4x4 byte transpose inside
-          // each quad of lanes (the quad's lanes hold four adjacent columns)
-          const unsigned int w = ((unsigned int)qc[0] & 0xFFu) | (((unsigned int)qc[1] & 0xFFu) << 8) |
-                                 (((unsigned int)qc[2] & 0xFFu) << 16) | ((unsigned int)qc[3] << 24);
-          const unsigned int x = (unsigned int)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);
-          const unsigned int a = __builtin_amdgcn_perm(x, w, (lrow & 2) ? 0x03020706u : 0x05040100u);
-          const unsigned int y = (unsigned int)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
-          const unsigned int t = __builtin_amdgcn_perm(y, a, (lrow & 1) ? 0x03070105u : 0x06020400u);
-          __builtin_amdgcn_raw_buffer_store_b32(t, rsrc, o.voffq[j], q * 8 * (int)p.ldq, 0);
-        }
-      }
+      if constexpr (st == 4) asm volatile("" : "+v"(tcol[j]));
     } else {
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(o.cbase + (int64_t)(wm_s * WTM + i * 32) * p.ldc), 0, (int)kBufRecords,
@@ -1736,7 +1717,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   out_cur.qbase = p.Q;
   out_cur.pbase = p.rowmax;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) out_cur.voff[j] = out_cur.voffq[j] = kBufInvalid;
+  for (int j = 0; j < FN; ++j) out_cur.voff[j] = kBufInvalid;
   out_cur.sr_base = out_cur.rk_base = out_cur.sc_base = out_cur.iv_base = 0;
   out_cur.col0 = 0;
   out_cur.slot = 0;
@@ -1744,10 +1725,10 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // all sixteen with three or more slots (those loads were issued a stage
   // earlier), with two slots only the four of its k-step 3 (the loads share
   // that k-step and precede its stores).  MODE 1 drains without stores.
-  // MODE 1 drains without stores; MODE 2 stores at least one word per part
-  // (four per stage when its codes are packed, sixteen bytes otherwise).
-  constexpr int PREV_ST = MODE == 1 ? 0 : MODE == 2 ? (STAGES >= 3 ? 4 : 1) : (STAGES >= 3 ? 16 : 4);
-  constexpr int CUR_ST = MODE == 1 ? 0 : MODE == 2 ? 3 : 12;   // stores of k-steps 0-2 of a draining stage
+  // MODE 1 drains without stores; MODE 2 stores its codes one byte per
+  // element, as many stores as MODE 0.
+  constexpr int PREV_ST = MODE == 1 ? 0 : (STAGES >= 3 ? 16 : 4);
+  constexpr int CUR_ST = MODE == 1 ? 0 : 12;   // stores of k-steps 0-2 of a draining stage
   auto run_tile = [&](v16i (&X)[FM][FN], v16i (&Y)[FM][FN], int r, auto DRAIN)
       __attribute__((always_inline)) {
     constexpr bool D = decltype(DRAIN)::value;
@@ -1886,26 +1867,12 @@ gemm_i8_persist128_kernel(const GemmParams p) {
       const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(out_cur.qbase + (int64_t)(wm_s * WTM + i * 32) * p.ldq), 0, (int)kBufRecords, 0x00020000);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int c4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = q * 8 + e;
-          float y = epilogue1(acc0[i][j][q * 4 + e], srp[rr], sc);
-          if (RELU) y = relu_pos0(y);
-          c4[e] = quantize1(y, ivp[rr]);
-          if (!p.qvec)
-            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)c4[e], rq, out_cur.voff[j], rr * (int)p.ldq, 0);
-        }
-        if (p.qvec) {   // the quad transpose of the drain
-          const unsigned int w = ((unsigned int)c4[0] & 0xFFu) | (((unsigned int)c4[1] & 0xFFu) << 8) |
-                                 (((unsigned int)c4[2] & 0xFFu) << 16) | ((unsigned int)c4[3] << 24);
-          const unsigned int x = (unsigned int)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);
-          const unsigned int a = __builtin_amdgcn_perm(x, w, (lrow & 2) ? 0x03020706u : 0x05040100u);
-          const unsigned int y = (unsigned int)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
-          const unsigned int t = __builtin_amdgcn_perm(y, a, (lrow & 1) ? 0x03070105u : 0x06020400u);
-          __builtin_amdgcn_raw_buffer_store_b32(t, rq, out_cur.voffq[j], q * 8 * (int)p.ldq, 0);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int rr = (v >> 2) * 8 + (v & 3);
+        float y = epilogue1(acc0[i][j][v], srp[rr], sc);
+        if (RELU) y = relu_pos0(y);
+        const int qv = quantize1(y, ivp[rr]);
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)qv, rq, out_cur.voff[j], rr * (int)p.ldq, 0);
       }
       return;
     }

@@ -31,7 +31,6 @@ struct GemmParams {
   unsigned int* rowmax;             // non-persistent: M words, zero before pass 1;
                                     // persistent: [tiles_n * 2][M] partial maxima
   const float* inv_row;             // persistent pass 2: RN(1/s) of every output row scale s
-  int qvec;                         // persistent pass 2: Q, ldq and N multiples of 4 (codes stored 4 per lane)
   int8_t* Q;                        // pass 2: codes, row-major, leading dimension ldq
   int64_t ldq;
   float* s_out;                     // pass 2: the M row scales of the codes

@@ -104,8 +104,8 @@ def test_requant_persistent(g, M, N, K, relu):
 @pytest.mark.parametrize("pad", [52, 53])
 def test_requant_persistent_padded_ldq(g, pad):
     """Codes written with a leading dimension larger than N: the padding
-    bytes between rows are left as they were (pad 52: codes stored four per
-    lane; pad 53, an odd leading dimension: one byte per lane)."""
+    bytes between rows are left as they were (an even and an odd leading
+    dimension)."""
     M, N, K = 512, 300, 768
     say("requant persistent ldq", M, N, K, pad)
     (QA, sA, QB, sB), (dQA, dsA, dQB, dsB) = _operands(g, M, N, K, 515)
