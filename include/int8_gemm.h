@@ -436,7 +436,9 @@ int i8g_probe_hash(uint64_t seed, int64_t M, int64_t N, int64_t K, uint64_t* has
  * planner's column quantize path, 1 = the two-pass kernels, 2 = the
  * cooperative one-read kernel wherever the shape allows it (see
  * quantize_cols), 3 = the two whole-line passes wherever the shape allows
- * them (the cooperative path's shapes); int4_direct: 1 = int4 GEMM operands read packed by the
+ * them (the cooperative path's shapes), 4 = the cooperative kernel with
+ * every wait cut to one spin (its timeout paths: a band whose exchange
+ * does not complete at once is left with NaN scales); int4_direct: 1 = int4 GEMM operands read packed by the
  * direct int4 kernel.  All zero / -1 restores the default.  Errors:
  * I8G_EINVAL for out-of-range values.
  */

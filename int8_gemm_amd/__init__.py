@@ -447,8 +447,9 @@ def plan_overrides(**kw):
     """Plan overrides for tests (i8g_set_test_overrides) inside a with-block:
     force_tile (-1: the planner's choice), force_splits (0: the planner's),
     qcols_path (0: the planner's, 1: two-pass kernels, 2: cooperative
-    one-read kernel, 3: two whole-line passes; 2 and 3 where the shape
-    allows them), int4_direct.  Blocks nest: settings not given are kept
+    one-read kernel, 3: two whole-line passes, 4: the cooperative kernel
+    with its waits cut to one spin; 2 to 4 where the shape allows them),
+    int4_direct.  Blocks nest: settings not given are kept
     from the enclosing block, and each block restores the previous ones."""
     unknown = set(kw) - set(_overrides)
     if unknown:

@@ -361,7 +361,7 @@ int gemm_i8_blockscaled(const int8_t* QA, int64_t lda, const float* s_row, const
 int i8g_set_test_overrides(int32_t force_tile, int32_t force_splits, int32_t qcols_path,
                            int32_t int4_direct) {
   if (force_tile < -1 || force_tile >= kNumGemmCfgs || force_splits < 0 || force_splits > 64 ||
-      qcols_path < 0 || qcols_path > 3)
+      qcols_path < 0 || qcols_path > 4)
     return I8G_EINVAL;
   set_test_overrides(force_tile, force_splits, qcols_path, int4_direct ? 1 : 0);
   return I8G_OK;

@@ -352,7 +352,11 @@ qcols_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int6
 // writes their codes (an atomic exchange) only after the other members have
 // left the wait (each adds 1 more, so the count reaches 2P-1).  All waits
 // are bounded; a member whose wait times out (the grid was not resident)
-// stops waiting for the rest of the launch and leaves the band's scales NaN.
+// stops waiting for the rest of the launch and leaves the band's scales NaN;
+// so does member 0 when its wait for the other members to leave (before it
+// writes the counter word's codes) times out.  The spin limit is a kernel
+// argument: kQkWaitLimit, or 0 under the test override that exercises these
+// paths.
 // Requires rows % 256 == 0, rows >= 1024, cols % 32 == 0, X and Qt 16-byte
 // aligned, ldx % 4 == 0, ldqt % 16 == 0 and 1024 rows of X addressable with
 // 32-bit offsets.
@@ -376,7 +380,7 @@ template <int FMT>
 __global__ void __launch_bounds__(QK_THREADS, 4)
 qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
                   int8_t* __restrict__ Qt, int64_t ldqt, float* __restrict__ scale, int P, int NG,
-                  int64_t nbands) {
+                  int64_t nbands, unsigned int wait_limit) {
   __shared__ float red[8][QK_COLS];
   __shared__ float s_inv[QK_COLS];
   __shared__ int s_ok;
@@ -393,17 +397,27 @@ qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
   const int vo = (4 * rg) * ld4 + slot * 16;           // rows 4*rg + e + 256*i of the chunk
   bool timed_out = false;
   unsigned int* pend_addr = nullptr;                   // member 0's counter word, codes pending
+  unsigned int* pend_sbits = nullptr;                  // ... and that band's scales
   unsigned int pend_codes = 0;
   auto settle = [&](bool block) __attribute__((always_inline)) {
     if (t != 0 || pend_addr == nullptr) return;
     unsigned int n = 0;
+    bool left = true;
     while (__hip_atomic_load(pend_addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
            (unsigned int)(2 * P - 1)) {
       if (!block && n >= 64) return;                   // again after the next band
       __builtin_amdgcn_s_sleep(2);
-      if (++n > kQkWaitLimit) break;
+      if (++n > wait_limit) {
+        left = false;
+        break;
+      }
     }
     __hip_atomic_exchange(pend_addr, pend_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a member still to leave may add to the word after the codes: the band
+    // is marked as failed
+    if (!left)
+      for (int k = 0; k < QK_COLS; ++k)
+        __hip_atomic_exchange(pend_sbits + k, 0x7FC00000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     pend_addr = nullptr;
   };
   for (int64_t b = g; b < nbands; b += NG) {
@@ -469,7 +483,7 @@ qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
         ok = true;
         while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned int)P) {
           __builtin_amdgcn_s_sleep(1);
-          if (++n > kQkWaitLimit) {
+          if (++n > wait_limit) {
             ok = false;
             break;
           }
@@ -522,6 +536,7 @@ qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
             d[2] = a2;
             d[3] = a3;
             pend_addr = d;                               // d[0] is the counter
+            pend_sbits = sbits;
             pend_codes = a0;
           } else {
             *reinterpret_cast<uint4*>(dst + qq * 16) = make_uint4(a0, a1, a2, a3);
@@ -665,7 +680,7 @@ static bool qcols_takes_coop(const float* X, int64_t rows, int64_t cols, int64_t
                              int64_t ldqt, int fmt) {
   const int path = qcols_path_requested();
   if (path == 1 || path == 3 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
-  return path == 2 || (double)rows * (double)cols * 4.0 >= kQkMinBytes;
+  return path == 2 || path == 4 || (double)rows * (double)cols * 4.0 >= kQkMinBytes;
 }
 
 // The two whole-line passes (qcols_lines_*), for tall and narrow inputs:
@@ -676,7 +691,7 @@ static bool qcols_takes_coop(const float* X, int64_t rows, int64_t cols, int64_t
 static bool qcols_takes_lines(const float* X, int64_t rows, int64_t cols, int64_t ldx, const int8_t* Qt,
                               int64_t ldqt, int fmt) {
   const int path = qcols_path_requested();
-  if (path == 1 || path == 2 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
+  if (path == 1 || path == 2 || path == 4 || !qcols_coop_shape_ok(X, rows, cols, ldx, Qt, ldqt, fmt)) return false;
   return path == 3 || (rows >= 4096 && cols <= 1024);
 }
 
@@ -716,7 +731,9 @@ static hipError_t launch_qcols_coop(const float* X, int64_t rows, int64_t cols, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int p = P, ng = (int)NG;
-  void* args[] = {&X, &rows, &cols, &ldx, &Qt, &ldqt, &scale, &p, &ng, const_cast<int64_t*>(&nbands)};
+  // the test override 4 cuts every wait to one spin (the timeout paths)
+  unsigned int wait_limit = qcols_path_requested() == 4 ? 0u : kQkWaitLimit;
+  void* args[] = {&X, &rows, &cols, &ldx, &Qt, &ldqt, &scale, &p, &ng, const_cast<int64_t*>(&nbands), &wait_limit};
   e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(qcols_coop_kernel<FMT>), dim3((unsigned int)(NG * P)),
                                  dim3(QK_THREADS), args, 0, stream);
   return e;

@@ -99,6 +99,9 @@ def test_test_overrides_and_plan_query():
     assert lib.i8g_set_test_overrides(8, 0, 0, 0) == 1        # no tile configuration 8
     assert lib.i8g_set_test_overrides(-2, 0, 0, 0) == 1
     assert lib.i8g_set_test_overrides(-1, -1, 0, 0) == 1
+    assert lib.i8g_set_test_overrides(-1, 0, 5, 0) == 1        # column paths 0..4
+    assert lib.i8g_set_test_overrides(-1, 0, 4, 0) == 0
+    assert lib.i8g_set_test_overrides(-1, 0, 0, 0) == 0
     with pytest.raises(g.I8GError):
         g.plan_query(0, 5, 5)
     free_cfg, free_splits = g.plan_query(1000, 1000, 1024)
