@@ -126,14 +126,35 @@ static float epilogue(int32_t acc, float sr, float sc, bool relu) {
   if (relu) y = y > 0.0f ? y : 0.0f;
   return y;
 }
+// The output hash of include/int8_gemm.h (output_hash), written here from
+// that definition on its own, without the device code's key functions, and
+// summed row by row where the kernels sum column by column: the gate's
+// hash check does not share code with the path it checks.
+static uint64_t mirror_fmix64(uint64_t k) {
+  const uint64_t m1 = 0xFF51AFD7ED558CCDull, m2 = 0xC4CEB9FE1A85EC53ull;
+  k = (k ^ (k >> 33)) * m1;
+  k = (k ^ (k >> 33)) * m2;
+  return k ^ (k >> 33);
+}
+static uint64_t mirror_row_key(uint64_t i) {
+  uint64_t x = i % 2147483648ull;   // i mod 2^31, then products mod 2^31
+  x ^= x >> 16;
+  x = (x * 0x3B9C5A1Dull) % 2147483648ull;
+  x ^= x >> 13;
+  x = (x * 0x2F6E8B35ull) % 2147483648ull;
+  x ^= x >> 16;
+  return 2 * x + 1;
+}
 static uint64_t hash_of(const float* C, int64_t M, int64_t N) {
+  std::vector<uint64_t> ck((size_t)N);
+  for (int64_t j = 0; j < N; ++j) ck[(size_t)j] = mirror_fmix64((uint64_t)j + 0x9E3779B97F4A7C15ull) | 1ull;
   uint64_t S = 0;
-  for (int64_t j = 0; j < N; ++j) {
-    uint64_t t = 0;
-    for (int64_t i = 0; i < M; ++i) t += (uint64_t)hash_row_key((uint32_t)i) * to_bits(C[i * N + j]);
-    S += hash_col_key((uint64_t)j) * t;
+  for (int64_t i = 0; i < M; ++i) {
+    uint64_t row = 0;
+    for (int64_t j = 0; j < N; ++j) row += ck[(size_t)j] * (uint64_t)to_bits(C[i * N + j]);
+    S += mirror_row_key((uint64_t)i) * row;
   }
-  return hash_finalize(S, (uint64_t)M, (uint64_t)N);
+  return mirror_fmix64(S ^ mirror_fmix64(((uint64_t)M << 32) + (uint64_t)N));
 }
 
 // Deterministic gate inputs: heavy-tailed values (a ratio of two uniforms)
