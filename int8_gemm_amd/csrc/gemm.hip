@@ -1622,6 +1622,12 @@ gemm_i8_persist128_kernel(const GemmParams p) {
   // its slots 0-3, before that stage's first epilogue stores.
   constexpr bool SPLIT = STAGES >= 3 && LPS > NSLOT;
   constexpr int LH = SPLIT ? NSLOT : LPS;
+  // MODE 1 with two workgroups per CU drains each tile right after its last
+  // k-step instead of under the next tile's MFMAs: no second accumulator set
+  // is live across the main loop (the interleaved drain's row maxima and
+  // both sets exceed the 256 registers of a wave at two waves per SIMD), and
+  // the other workgroup's MFMAs keep the SIMD busy meanwhile.
+  constexpr bool SYNC = MODE == 1 && WPC >= 2;
   auto kstep = [&](v16i (&X)[FM][FN], const v4i (&fa)[FM], const v4i (&fb)[FN], auto ZERO, int nbuf,
                    int nt, v4i (&na)[FM], v4i (&nb)[FN], auto DMA, const Dma& dm, bool dma_on, auto LB, auto LE,
                    auto&& slot)
@@ -1770,7 +1776,7 @@ gemm_i8_persist128_kernel(const GemmParams p) {
             read_late_early(out_prev, BI, late, out_cur, std::integral_constant<int, 0>(), en, sc_n);
           else
             read_late(out_prev, BI, late);
-        } else if constexpr (b + 1 == NB) {
+        } else if constexpr (b + 1 == NB && !SYNC) {
           if (nst == NB && has_next) read_early(out_cur, std::integral_constant<int, 0>(), en, sc_n);
         }
       };
@@ -1786,7 +1792,8 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     static_assert(NB % 2 == 0, "stage NB (if any) finds its next early half in e0");
     for (int s = NB; s < nst; ++s) {
       auto mid = [&]() __attribute__((always_inline)) {
-        if (s + 1 == nst && has_next) read_early(out_cur, std::integral_constant<int, 0>(), e0, s0);
+        if constexpr (!SYNC)
+          if (s + 1 == nst && has_next) read_early(out_cur, std::integral_constant<int, 0>(), e0, s0);
       };
       if (s == NB)
         stage(X, Y, g0 + s, out_prev, e0, s0, late, std::false_type(), std::false_type(),
@@ -1795,6 +1802,40 @@ gemm_i8_persist128_kernel(const GemmParams p) {
         stage(X, Y, g0 + s, out_prev, e0, s0, late, std::false_type(), std::false_type(),
               std::integral_constant<int, 0>(), std::integral_constant<int, (STAGES - 2) * LPS>(), mid);
     }
+  };
+
+  // SYNC: the row maxima of tile o (in acc0) right after its last k-step.
+  // Loads of later stages may still be landing in LDS, so the scales are
+  // read by asm statements that wait for the LDS reads only.
+  auto sync_max = [&](const Out& o) __attribute__((always_inline)) {
+    static_for<0, FM>([&](auto II) __attribute__((always_inline)) {
+      constexpr int i = decltype(II)::value;
+      v4i sr[4];
+      asm volatile(
+          "ds_read_b128 %[s0], %[sr] offset:%[o0]\n\t"
+          "ds_read_b128 %[s1], %[sr] offset:%[o1]\n\t"
+          "ds_read_b128 %[s2], %[sr] offset:%[o2]\n\t"
+          "ds_read_b128 %[s3], %[sr] offset:%[o3]\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : [s0] "=&v"(sr[0]), [s1] "=&v"(sr[1]), [s2] "=&v"(sr[2]), [s3] "=&v"(sr[3])
+          : [sr] "v"(o.sr_base), [o0] "i"(i * 128), [o1] "i"(i * 128 + 32), [o2] "i"(i * 128 + 64),
+            [o3] "i"(i * 128 + 96));
+      static_for<0, FN>([&](auto JJ) __attribute__((always_inline)) {
+        constexpr int j = decltype(JJ)::value;
+        int sc;
+        asm volatile("ds_read_b32 %[sc], %[sca] offset:%[oc]\n\ts_waitcnt lgkmcnt(0)"
+                     : [sc] "=&v"(sc)
+                     : [sca] "v"(o.sc_base), [oc] "i"(j * 128));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float y = epilogue1(acc0[i][j][v], __int_as_float(sr[v >> 2][v & 3]), __int_as_float(sc));
+          if (RELU) y = relu_pos0(y);
+          const unsigned int a = __float_as_uint(y) & 0x7FFFFFFFu;
+          rmx[i][v] = a > rmx[i][v] ? a : rmx[i][v];
+        }
+      });
+    });
+    close_tile_max(o);
   };
 
   if (my_tiles > 0) {
@@ -1815,16 +1856,26 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     for (int j = 0; j < FN; ++j) tcol[j] = 0;
 
     run_tile(acc0, acc1, 0, std::false_type());
-    for (int r = 1; r < my_tiles; ++r) {
+    if constexpr (SYNC) {
+      for (int r = 1; r < my_tiles; ++r) {
+        sync_max(out_cur);
+        int a, b;
+        tile_coords(r, a, b);
+        make_out(r, a, b, out_cur);
+        run_tile(acc0, acc1, r, std::false_type());
+      }
+    } else {
+      for (int r = 1; r < my_tiles; ++r) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc1[i][j] = acc0[i][j];
-      out_prev = out_cur;
-      int a, b;
-      tile_coords(r, a, b);
-      make_out(r, a, b, out_cur);
-      run_tile(acc0, acc1, r, std::true_type());
+          for (int j = 0; j < FN; ++j) acc1[i][j] = acc0[i][j];
+        out_prev = out_cur;
+        int a, b;
+        tile_coords(r, a, b);
+        make_out(r, a, b, out_cur);
+        run_tile(acc0, acc1, r, std::true_type());
+      }
     }
     // The last tile: no MFMAs left to hide its epilogue under.  Its hash
     // terms come first and its stores last, so that publishing this
@@ -1832,7 +1883,9 @@ gemm_i8_persist128_kernel(const GemmParams p) {
     // and vmcnt retires in order) does not wait behind the tile's stores.
     // Every direct-to-LDS load has landed here, so plain LDS reads are used.
     wait_vmcnt<0>();
-    if constexpr (MODE == 1) {
+    if constexpr (SYNC) {
+      sync_max(out_cur);
+    } else if constexpr (MODE == 1) {
       static_for<0, NB>([&](auto BI) __attribute__((always_inline)) {
         constexpr int b = decltype(BI)::value, i = b / FN, j = b % FN;
         const int r0 = wm * WTM + i * 32 + lhalf * 4;
@@ -2277,8 +2330,8 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
 // requantizing epilogue: pass 1 (row maxima of |y|), the row scales, pass 2
 // (codes, hash).  Both passes run the same tile walk and the same exact
 // contraction, so pass 2 sees exactly the y that pass 1 reduced.
-//  * Persistent (the 128x192 tile with 128-byte stages, where the shape
-//    allows it): pass 1 stores each wave's partial maximum of every row of
+//  * Persistent (the 128x128 tile with two workgroups per CU for K <= 1024,
+//    else the 128x192 tile; 128-byte stages): pass 1 stores each wave's partial maximum of every row of
 //    its tile (no atomics: [tiles_n * 2][M] words), requant_scales_kernel
 //    reduces them to the row scales and their reciprocals, and pass 2 loads
 //    the reciprocals into the tile's scale slot beside the row and column
@@ -2319,13 +2372,19 @@ __global__ void __launch_bounds__(256) requant_scales_kernel(const unsigned int*
   }
 }
 
-constexpr int kRequantPersistCfg = 6;
+// The persistent tiles of the two passes, in order of preference: 128x128
+// with two workgroups per CU (K <= 1024), then 128x192.
+constexpr int kRequantPersistCfgs[2] = {7, 6};
 
 GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K, int64_t ldq) {
   int force = g_force_tile.load(std::memory_order_relaxed);
-  if ((force < 0 || force == kRequantPersistCfg) && ldq <= (int64_t(1) << 24)) {
-    const GemmPlan pp = plan_gemm_forced(M, N, K, true, kRequantPersistCfg, 1);
-    if (pp.cfg == kRequantPersistCfg) return pp;
+  if (ldq <= (int64_t(1) << 24)) {
+    for (const int c : kRequantPersistCfgs) {
+      if (force >= 0 && force != c) continue;
+      if (c == 7 && K > 1024) continue;
+      const GemmPlan pp = plan_gemm_forced(M, N, K, true, c, 1);
+      if (pp.cfg == c) return pp;
+    }
   }
   if (force > 2) force = -1;
   return plan_gemm_forced(M, N, K, false, force, 1);
@@ -2374,12 +2433,19 @@ static void launch_persist_mode(const GemmParams& p, unsigned int grid, hipStrea
 hipError_t launch_gemm_requant(GemmParams p, const GemmPlan& plan, const RequantLayout& l, hipStream_t stream) {
   const int do_hash = p.do_hash;
   if (plan.persistent) {
+    const bool t7 = plan.cfg == 7;
     p.do_hash = 0;
-    launch_persist_mode<1, 128, 192, 3, 1>(p, (unsigned int)plan.grid, stream);
+    if (t7)
+      launch_persist_mode<1, 128, 128, 2, 2>(p, (unsigned int)plan.grid, stream);
+    else
+      launch_persist_mode<1, 128, 192, 3, 1>(p, (unsigned int)plan.grid, stream);
     hipLaunchKernelGGL(requant_scales_kernel, dim3((unsigned int)((p.M + 63) / 64)), dim3(256), 0, stream,
                        p.rowmax, l.partials, p.M, p.s_out, const_cast<float*>(p.inv_row));
     p.do_hash = do_hash;
-    launch_persist_mode<2, 128, 192, 3, 1>(p, (unsigned int)plan.grid, stream);
+    if (t7)
+      launch_persist_mode<2, 128, 128, 2, 2>(p, (unsigned int)plan.grid, stream);
+    else
+      launch_persist_mode<2, 128, 192, 3, 1>(p, (unsigned int)plan.grid, stream);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned int)((p.M + 255) / 256)), dim3(256), 0, stream,

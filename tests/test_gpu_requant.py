@@ -101,6 +101,38 @@ def test_requant_persistent(g, M, N, K, relu):
     assert g.hash_value(h) == g.hash_value(h2)
 
 
+# shapes with K <= 1024, which the 128x128 passes with two workgroups per CU
+# take by default: ragged last column tile, more tiles than workgroups, K of
+# 7 and 8 stages
+T7_SHAPES = [s for s in PERSIST_SHAPES if s[2] <= 1024] + [(512, 384, 1024, True), (4096, 2100, 768, False)]
+
+
+@pytest.mark.parametrize("M,N,K,relu", T7_SHAPES)
+def test_requant_persistent_two_per_cu(g, M, N, K, relu):
+    """The 128x128 passes (two workgroups per CU; pass 1 reduces each tile's
+    row maxima right after the tile's last k-step) against the oracle and
+    against the 128x192 passes, bit for bit."""
+    say("requant persistent 128x128", M, N, K, relu)
+    (QA, sA, QB, sB), dev = _operands(g, M, N, K, M * 5 + N + K)
+    Qw, sw, Cw = requant.gemm_requant(QA, sA, QB, sB, relu)
+    lib = g.load()
+    # the planner's choice for these shapes: one partial maximum per row for
+    # each wave column of each 128-column tile
+    assert lib.gemm_i8_requant_workspace_bytes(M, N, K) >= M * 4 * 2 * -(-N // 128)
+    with g.plan_overrides(force_tile=7):
+        assert lib.gemm_i8_requant_workspace_bytes(M, N, K) >= M * 4 * 2 * -(-N // 128)
+        Q, s, h = g.gemm_i8_requant(*dev, relu=relu, want_hash=True)
+        torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(Q.cpu().numpy(), Qw)
+    assert g.hash_value(h) == hashref.output_hash(Cw)
+    with g.plan_overrides(force_tile=6):
+        Q6, s6, h6 = g.gemm_i8_requant(*dev, relu=relu, want_hash=True)
+        torch.cuda.synchronize()
+    assert torch.equal(Q, Q6) and torch.equal(s.view(torch.int32), s6.view(torch.int32))
+    assert g.hash_value(h) == g.hash_value(h6)
+
+
 @pytest.mark.parametrize("pad", [52, 53])
 def test_requant_persistent_padded_ldq(g, pad):
     """Codes written with a leading dimension larger than N: the padding
