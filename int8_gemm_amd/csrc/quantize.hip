@@ -522,12 +522,14 @@ qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
     }
     __syncthreads();
     {
-      const int jj = t >> 4, part = t & 15;             // Qt row b*32+jj, bytes part*64 .. +64
-      int8_t* dst = Qt + (b * QK_COLS + jj) * ldqt + r0 + part * 64;
+      // Qt row b*32+jj, bytes qq*256 + part*16 .. +16: the 16 lanes of a row
+      // store 256 contiguous bytes per instruction
+      const int jj = t >> 4, part = t & 15;
+      int8_t* dst = Qt + (b * QK_COLS + jj) * ldqt + r0 + part * 16;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int w = part * 16 + qq * 4;
-        if (r0 + part * 64 + qq * 16 < rows) {           // rows % 256 == 0: whole 16-byte groups
+        const int w = qq * 64 + part * 4;
+        if (r0 + qq * 256 + part * 16 < rows) {          // rows % 256 == 0: whole 16-byte groups
           const unsigned int a0 = tile[jj][w], a1 = tile[jj][w + 1], a2 = tile[jj][w + 2], a3 = tile[jj][w + 3];
           if (m == 0 && jj == 0 && part == 0 && qq == 0) {
             settle(true);                                // the previous band's word first
@@ -539,7 +541,7 @@ qcols_coop_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
             pend_sbits = sbits;
             pend_codes = a0;
           } else {
-            *reinterpret_cast<uint4*>(dst + qq * 16) = make_uint4(a0, a1, a2, a3);
+            *reinterpret_cast<uint4*>(dst + qq * 256) = make_uint4(a0, a1, a2, a3);
           }
         }
       }
@@ -658,13 +660,15 @@ qcols_lines_quant_kernel(const float* __restrict__ X, int64_t rows, int64_t ldx,
     tile[slot * 4 + 3][rg + 64 * i] = w3;
   }
   __syncthreads();
-  const int jj = t >> 4, part = t & 15;                 // Qt row b*32+jj, bytes part*64 .. +64
-  int8_t* dst = Qt + (b * QK_COLS + jj) * ldqt + r0 + part * 64;
+  // Qt row b*32+jj, bytes qq*256 + part*16 .. +16 (256 contiguous bytes per
+  // row and instruction)
+  const int jj = t >> 4, part = t & 15;
+  int8_t* dst = Qt + (b * QK_COLS + jj) * ldqt + r0 + part * 16;
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
-    const int w = part * 16 + qq * 4;
-    if (r0 + part * 64 + qq * 16 < rows)                 // rows % 256 == 0: whole 16-byte groups
-      *reinterpret_cast<uint4*>(dst + qq * 16) = make_uint4(tile[jj][w], tile[jj][w + 1], tile[jj][w + 2], tile[jj][w + 3]);
+    const int w = qq * 64 + part * 4;
+    if (r0 + qq * 256 + part * 16 < rows)                // rows % 256 == 0: whole 16-byte groups
+      *reinterpret_cast<uint4*>(dst + qq * 256) = make_uint4(tile[jj][w], tile[jj][w + 1], tile[jj][w + 2], tile[jj][w + 3]);
   }
 }
 
