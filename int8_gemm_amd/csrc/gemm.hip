@@ -2013,7 +2013,6 @@ constexpr int COMB_ROWS_MAX = 32;
 __global__ void __launch_bounds__(256)
 splitk_combine_kernel(const GemmParams p) {
   __shared__ unsigned long long red[4];
-  __shared__ int last_flag;
   const int M = p.M, N = p.N;
   const int tid = threadIdx.x;
   const int c0 = (blockIdx.x * 256 + tid) * 4;
@@ -2030,7 +2029,22 @@ splitk_combine_kernel(const GemmParams p) {
     for (int r = r0; r < r1; ++r) {
       int a[4] = {0, 0, 0, 0};
       const int* src = p.partials + (int64_t)r * N + c0;
-      for (int sp = 0; sp < p.splits; ++sp) {
+      int sp = 0;
+      if (vec) {
+        // four splits' loads in flight together (integer sums: exact in any
+        // order)
+        for (; sp + 4 <= p.splits; sp += 4) {
+          v4i v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + (sp + u) * plane));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            a[0] += v[u][0]; a[1] += v[u][1]; a[2] += v[u][2]; a[3] += v[u][3];
+          }
+        }
+      }
+      for (; sp < p.splits; ++sp) {
         if (vec) {
           const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + sp * plane));
           a[0] += v[0]; a[1] += v[1]; a[2] += v[2]; a[3] += v[3];
@@ -2059,16 +2073,37 @@ splitk_combine_kernel(const GemmParams p) {
       }
     }
   }
-  uint64_t part = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (c0 + e < N) part += hash_col_key((uint64_t)(c0 + e)) * t[e];
   if (p.do_hash) {
+    uint64_t part = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c0 + e < N) part += hash_col_key((uint64_t)(c0 + e)) * t[e];
+    // this workgroup's share; hash_parts_finalize_kernel, the next launch,
+    // sums the shares (no cross-workgroup wait at the end of this kernel,
+    // whose workgroups all finish together)
     part = block_sum_u64<256>(part, red);
-    hash_share_and_finalize<256>(part, p.hash_parts, p.ticket, p.n_shares,
-                                 blockIdx.y * gridDim.x + blockIdx.x, (uint64_t)M, (uint64_t)N,
-                                 p.hash_out, red, &last_flag);
+    if (tid == 0) p.hash_parts[blockIdx.y * gridDim.x + blockIdx.x] = part;
   }
+}
+
+// H from the n shares of S written by the previous launch.
+__global__ void __launch_bounds__(256)
+hash_parts_finalize_kernel(const unsigned long long* __restrict__ parts, int n, uint64_t M, uint64_t N,
+                           uint64_t* hash_out) {
+  __shared__ unsigned long long red[4];
+  uint64_t s = 0;
+  for (int i0 = 0; i0 < n; i0 += 256 * 8) {   // eight loads in flight per thread
+    uint64_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = i0 + k * 256 + (int)threadIdx.x;
+      v[k] = i < n ? parts[i] : 0ull;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  s = block_sum_u64<256>(s, red);
+  if (threadIdx.x == 0) *hash_out = hash_finalize(s, M, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -2320,8 +2355,12 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
       launch_persist128<128, 192, 3, 1>(p, grid, stream);
       break;
   }
-  if (plan.splits > 1)
+  if (plan.splits > 1) {
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(plan.comb_x, plan.comb_y), dim3(256), 0, stream, p);
+    if (p.do_hash)
+      hipLaunchKernelGGL(hash_parts_finalize_kernel, dim3(1), dim3(256), 0, stream, p.hash_parts,
+                         plan.comb_x * plan.comb_y, (uint64_t)p.M, (uint64_t)p.N, p.hash_out);
+  }
   return hipGetLastError();
 }
 
