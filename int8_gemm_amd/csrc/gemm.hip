@@ -2106,6 +2106,13 @@ hash_parts_finalize_kernel(const unsigned long long* __restrict__ parts, int n, 
   if (threadIdx.x == 0) *hash_out = hash_finalize(s, M, N);
 }
 
+hipError_t launch_hash_parts_finalize(const unsigned long long* parts, int n, int64_t M, int64_t N,
+                                      uint64_t* hash_out, hipStream_t stream) {
+  hipLaunchKernelGGL(hash_parts_finalize_kernel, dim3(1), dim3(256), 0, stream, parts, n, (uint64_t)M,
+                     (uint64_t)N, hash_out);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // host side: plan and launch
 // ---------------------------------------------------------------------------
@@ -2358,8 +2365,7 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
   if (plan.splits > 1) {
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(plan.comb_x, plan.comb_y), dim3(256), 0, stream, p);
     if (p.do_hash)
-      hipLaunchKernelGGL(hash_parts_finalize_kernel, dim3(1), dim3(256), 0, stream, p.hash_parts,
-                         plan.comb_x * plan.comb_y, (uint64_t)p.M, (uint64_t)p.N, p.hash_out);
+      launch_hash_parts_finalize(p.hash_parts, plan.comb_x * plan.comb_y, p.M, p.N, p.hash_out, stream);
   }
   return hipGetLastError();
 }

@@ -146,6 +146,10 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
 hipError_t launch_quantize_batch(QJob* jobs, int n, hipStream_t stream);
 hipError_t launch_output_hash(const float* C, int64_t M, int64_t N, int64_t ldc,
                               uint64_t* hash, void* workspace, hipStream_t stream);
+// H from n shares of S that an earlier launch on `stream` stored at parts
+// (a one-workgroup kernel).
+hipError_t launch_hash_parts_finalize(const unsigned long long* parts, int n, int64_t M, int64_t N,
+                                      uint64_t* hash_out, hipStream_t stream);
 
 // Workspace layout shared by every call: a 256-byte header (word 0 is the
 // share ticket, zero between calls), then 8-byte hash shares, then (GEMM
