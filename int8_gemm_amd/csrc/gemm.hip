@@ -80,8 +80,11 @@ __device__ __forceinline__ void map_workgroup(int wg, int total, int tiles_m, in
   const int xcd = wg & 7, idx = wg >> 3;
   const int per = total >> 3, rem = total & 7;
   const int w = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  split = w % splits;
-  const int tile = w / splits;
+  // split-major: the workgroups of one XCD work on one K range, tiles in
+  // GROUP_M order inside it, so they share A and B slices in their L2
+  const int tiles = tiles_m * tiles_n;
+  split = w / tiles;
+  const int tile = w - split * tiles;
   const int group_size = GROUP_M * tiles_n;
   const int group = tile / group_size;
   const int first_m = group * GROUP_M;
