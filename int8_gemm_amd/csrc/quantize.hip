@@ -66,6 +66,37 @@ __device__ __forceinline__ void store4(int8_t* row, int64_t c, int64_t cols, uns
 // The kernel bodies take the workgroup's index within their own grid (`bid`)
 // and their LDS from the caller, so that quantize_batch_kernel can run
 // several of them in one launch.
+// A row of `cols` values (cols % 4 == 0, X rows 16-byte aligned, Q rows
+// 4-byte aligned) by one wave, through buffer loads and stores from the
+// row's base (uniform in the wave): a lane keeps only the row's data and its
+// offset live, no 64-bit addresses; groups past the row's end read as zeros
+// and store nothing.
+template <int VPL, int FMT>
+__device__ __forceinline__ void qrows_wave_vec_body(const float* __restrict__ X, int64_t cols, int64_t ldx,
+                                                    int8_t* __restrict__ Q, int64_t ldq,
+                                                    float* __restrict__ scale, int64_t r) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(uniform_ptr(X + r * ldx)), 0, (int)(cols * 4), 0x00020000);
+  float4 v[VPL];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const v4f x = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * 16, i * 1024, 0));
+    v[i] = make_float4(x[0], x[1], x[2], x[3]);
+    m = absmax4(m, v[i]);
+  }
+  m = wave_max_f32(m);
+  const float s = scale_of_absmax_fmt<FMT>(m);
+  const float inv = recip_rn(s);
+  if (lane == 0) scale[r] = s;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(Q + r * ldq), 0, (int)cols, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) __builtin_amdgcn_raw_buffer_store_b32(pack4(v[i], inv), rq, lane * 4, i * 256, 0);
+}
+
 template <int VPL, int FMT>
 __device__ __forceinline__ void qrows_wave_body(const float* __restrict__ X, int64_t rows, int64_t cols,
                                                 int64_t ldx, int8_t* __restrict__ Q, int64_t ldq,
@@ -77,6 +108,10 @@ __device__ __forceinline__ void qrows_wave_body(const float* __restrict__ X, int
   const float* xr = X + r * ldx;
   float4 v[VPL];
   float m = 0.0f;
+  if (vec_in && vec_out && (cols & 3) == 0) {
+    qrows_wave_vec_body<VPL, FMT>(X, cols, ldx, Q, ldq, scale, r);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     v[i] = load4(xr, (int64_t)(lane + 64 * i) * 4, cols, vec_in);
@@ -100,6 +135,28 @@ qrows_wave_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64
                   int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale, int vec_in,
                   int vec_out) {
   qrows_wave_body<VPL, FMT>(X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out, blockIdx.x);
+}
+
+// The same for aligned rows only: no per-element path in the kernel, so it
+// keeps fewer registers and more waves resident.
+template <int VPL, int FMT>
+__global__ void __launch_bounds__(256)
+qrows_wave_vec_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_t ldx,
+                      int8_t* __restrict__ Q, int64_t ldq, float* __restrict__ scale) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // a wave per row
+  if (r >= rows) return;
+  qrows_wave_vec_body<VPL, FMT>(X, cols, ldx, Q, ldq, scale, r);
+}
+
+template <int VPL, int FMT>
+static void launch_qrows_wave(dim3 grid, hipStream_t stream, const float* X, int64_t rows, int64_t cols,
+                              int64_t ldx, int8_t* Q, int64_t ldq, float* scale, int vec_in, int vec_out) {
+  if (vec_in && vec_out && (cols & 3) == 0)
+    hipLaunchKernelGGL((qrows_wave_vec_kernel<VPL, FMT>), grid, dim3(256), 0, stream, X, rows, cols, ldx, Q, ldq,
+                       scale);
+  else
+    hipLaunchKernelGGL((qrows_wave_kernel<VPL, FMT>), grid, dim3(256), 0, stream, X, rows, cols, ldx, Q, ldq,
+                       scale, vec_in, vec_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,21 +240,21 @@ hipError_t quantize_rows_int8(const float* X, int64_t rows, int64_t cols, int64_
   const int vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   const int vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
   if (rows_wave_vpl(cols) > 0) {
-    const dim3 grid((unsigned int)((rows + 3) / 4)), block(256);
+    const dim3 grid((unsigned int)((rows + 3) / 4));
     if (cols <= 256)
-      hipLaunchKernelGGL((qrows_wave_kernel<1, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<1, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 512)
-      hipLaunchKernelGGL((qrows_wave_kernel<2, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<2, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 768)
-      hipLaunchKernelGGL((qrows_wave_kernel<3, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<3, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 1024)
-      hipLaunchKernelGGL((qrows_wave_kernel<4, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<4, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 2048)
-      hipLaunchKernelGGL((qrows_wave_kernel<8, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<8, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else if (cols <= 3072)
-      hipLaunchKernelGGL((qrows_wave_kernel<12, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<12, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
     else
-      hipLaunchKernelGGL((qrows_wave_kernel<16, FMT>), grid, block, 0, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
+      launch_qrows_wave<16, FMT>(grid, stream, X, rows, cols, ldx, Q, ldq, scale, vec_in, vec_out);
   } else {
     const dim3 grid((unsigned int)rows), block(1024);
     if (rows_block_vpt(cols) == 8)
