@@ -26,8 +26,10 @@
 //  * The epilogue converts, scales (row scale, then column scale, separate
 //    roundings), applies ReLU as a select (so never -0), stores f32, and
 //    computes the tile's share of the output hash S = sum c(j)*r(i)*bits(i,j)
-//    mod 2^64; the workgroup that finishes last adds the shares (mod 2^64,
-//    any order) and writes H (see hash_share_and_finalize).
+//    mod 2^64; in the GEMM kernels the workgroup that finishes last adds the
+//    shares (mod 2^64, any order) and writes H (see hash_share_and_finalize);
+//    the split-K combine, whose workgroups all end together, stores its
+//    shares and a one-workgroup kernel launched after it adds them.
 #include <atomic>
 #include <cmath>
 #include <type_traits>
