@@ -2369,8 +2369,11 @@ hipError_t launch_gemm(const GemmParams& p, const GemmPlan& plan, hipStream_t st
   }
   if (plan.splits > 1) {
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(plan.comb_x, plan.comb_y), dim3(256), 0, stream, p);
-    if (p.do_hash)
-      launch_hash_parts_finalize(p.hash_parts, plan.comb_x * plan.comb_y, p.M, p.N, p.hash_out, stream);
+    if (p.do_hash) {
+      const hipError_t e =
+          launch_hash_parts_finalize(p.hash_parts, plan.comb_x * plan.comb_y, p.M, p.N, p.hash_out, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipGetLastError();
 }
