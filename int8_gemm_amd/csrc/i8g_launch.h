@@ -100,13 +100,13 @@ bool int4_direct_requested();
 // gemm_i4_kernel.  Process-wide.
 void set_test_overrides(int force_tile, int force_splits, int qcols_path, int int4_direct);
 int qcols_path_requested();
-// Requantizing epilogue: one K split, a non-persistent tile (a forced tile
-// 0..2 honoured for tests); the workspace adds M words of row maxima.
-// The requantizing epilogue's plan: the persistent 128x192 tile where the
-// shape allows it (K % 128 == 0, K >= 768, M % 128 == 0, ldq <= 2^24), else
-// a non-persistent tile.  Its workspace after the GEMM's own: the row maxima
-// (non-persistent: M words; persistent: `partials` x M words, then the M
-// reciprocals at inv_offset).
+// The requantizing epilogue's plan: one K split; a persistent tile where the
+// shape allows it (K % 128 == 0, K >= 768, M % 128 == 0, ldq <= 2^24: the
+// 128x128 tile with two workgroups per CU for K <= 1024, else 128x192), else
+// a non-persistent tile (a forced tile 0..2, 6 or 7 is honoured for tests).
+// Its workspace after the GEMM's own: the row maxima (non-persistent: M
+// words; persistent: `partials` x M words, then the M reciprocals at
+// inv_offset).
 GemmPlan plan_gemm_requant(int64_t M, int64_t N, int64_t K, int64_t ldq);
 struct RequantLayout {
   size_t max_offset, inv_offset, bytes;
