@@ -83,7 +83,7 @@ __device__ __forceinline__ void qrows_wave_vec_body(const float* __restrict__ X,
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const v4f x = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * 16, i * 1024, 0));
+    const v4f x = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * 16 + i * 1024, 0, 0));
     v[i] = make_float4(x[0], x[1], x[2], x[3]);
     m = absmax4(m, v[i]);
   }
@@ -94,7 +94,7 @@ __device__ __forceinline__ void qrows_wave_vec_body(const float* __restrict__ X,
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(Q + r * ldq), 0, (int)cols, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) __builtin_amdgcn_raw_buffer_store_b32(pack4(v[i], inv), rq, lane * 4, i * 256, 0);
+  for (int i = 0; i < VPL; ++i) __builtin_amdgcn_raw_buffer_store_b32(pack4(v[i], inv), rq, lane * 4 + i * 256, 0, 0);
 }
 
 template <int VPL, int FMT>
@@ -841,14 +841,35 @@ __device__ __forceinline__ void qcols_reg_body(const float* __restrict__ X, int6
 
   float4 v[QCR_VPT];
   float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  if (vec_in && (cols & 3) == 0 && (double)rows * (double)ldx * 4.0 < 2147483648.0) {
+    // buffer loads from the band's first column (uniform): 32-bit offsets
+    // instead of 64-bit addresses; a row at or past `rows`, or a column group
+    // past `cols`, gets an offset beyond the resource and reads as zeros
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(uniform_ptr(X + j0)), 0, (int)((rows - 1) * ldx * 4 + (cols - j0) * 4), 0x00020000);
+    const bool col_ok = j0 + cg * 4 < cols;
 #pragma unroll
-  for (int p = 0; p < QCR_VPT; ++p) {
-    const int64_t r = r_off + (int64_t)p * RPP;
-    v[p] = r < rows ? load4(X + r * ldx, j0 + cg * 4, cols, vec_in) : make_float4(0.f, 0.f, 0.f, 0.f);
-    m0 = fmaxf(m0, fabsf(v[p].x));
-    m1 = fmaxf(m1, fabsf(v[p].y));
-    m2 = fmaxf(m2, fabsf(v[p].z));
-    m3 = fmaxf(m3, fabsf(v[p].w));
+    for (int p = 0; p < QCR_VPT; ++p) {
+      const int64_t r = r_off + (int64_t)p * RPP;
+      const int vo = col_ok && r < rows ? (int)((r * ldx + cg * 4) * 4) : 0x7FFFFFFF;
+      const v4f x = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+      v[p] = make_float4(x[0], x[1], x[2], x[3]);
+      m0 = fmaxf(m0, fabsf(v[p].x));
+      m1 = fmaxf(m1, fabsf(v[p].y));
+      m2 = fmaxf(m2, fabsf(v[p].z));
+      m3 = fmaxf(m3, fabsf(v[p].w));
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < QCR_VPT; ++p) {
+      const int64_t r = r_off + (int64_t)p * RPP;
+      v[p] = r < rows ? load4(X + r * ldx, j0 + cg * 4, cols, vec_in) : make_float4(0.f, 0.f, 0.f, 0.f);
+      m0 = fmaxf(m0, fabsf(v[p].x));
+      m1 = fmaxf(m1, fabsf(v[p].y));
+      m2 = fmaxf(m2, fabsf(v[p].z));
+      m3 = fmaxf(m3, fabsf(v[p].w));
+    }
   }
   // lanes l, l+C4, l+2*C4, ... of a wave hold the same columns
 #pragma unroll
