@@ -61,8 +61,8 @@ def adversarial_inputs(c):
 # ---------------------------------------------------------------------------
 # quantize
 # ---------------------------------------------------------------------------
-QR_SHAPES = [(1, 1), (3, 5), (17, 300), (64, 768), (100, 1000), (9, 3072), (7, 4097),
-             (3, 5000), (2, 33000), (2, 70000)]
+QR_SHAPES = [(1, 1), (3, 5), (17, 300), (64, 768), (100, 1000), (6, 2044), (9, 3072), (5, 4000),
+             (7, 4097), (3, 5000), (2, 33000), (2, 70000)]
 
 
 def _quant_input(rows, cols, seed):
