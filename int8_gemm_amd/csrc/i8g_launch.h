@@ -122,9 +122,10 @@ hipError_t launch_quantize_rows(const float* X, int64_t rows, int64_t cols, int6
 hipError_t launch_quantize_cols(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                 int8_t* Qt, int64_t ldqt, float* scale, int fmt, hipStream_t stream);
 // One quantize pass of quantize_batch (planned by plan_qjob): a row pass
-// with a wave per row, a row pass with a workgroup per row, or a column pass
-// with a workgroup per band of columns.
-enum QKind : int { QK_ROWS_WAVE = 0, QK_ROWS_BLOCK = 1, QK_COLS_REG = 2 };
+// with a wave per row, a row pass with a workgroup per row, a column pass
+// with a workgroup per band of columns, or a pass over aligned rows of
+// 1025-3072 values with a wave per row (the vector body only).
+enum QKind : int { QK_ROWS_WAVE = 0, QK_ROWS_BLOCK = 1, QK_COLS_REG = 2, QK_ROWS_VEC = 3 };
 struct QJob {
   const float* X;
   int8_t* Q;

@@ -1183,7 +1183,14 @@ __device__ __forceinline__ void run_qjob(const QJob& q, int bid, char* smem) {
     }
     return;
   }
-  if (q.kind == QK_ROWS_WAVE) {
+  if (q.kind == QK_ROWS_VEC) {
+    const int64_t r = (int64_t)bid * (blockDim.x >> 6) + (threadIdx.x >> 6);   // a wave per row
+    if (r >= q.rows) return;
+    if (q.param == 8)
+      qrows_wave_vec_body<8, FMT>(q.X, q.cols, q.ldx, q.Q, q.ldq, q.scale, r);
+    else
+      qrows_wave_vec_body<12, FMT>(q.X, q.cols, q.ldx, q.Q, q.ldq, q.scale, r);
+  } else if (q.kind == QK_ROWS_WAVE) {
     switch (q.param) {
       case 1: qrows_wave_body<1, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
       case 2: qrows_wave_body<2, FMT>(q.X, q.rows, q.cols, q.ldx, q.Q, q.ldq, q.scale, q.vec_in, q.vec_out, bid); break;
@@ -1227,12 +1234,20 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
   q.vec_in = ((uintptr_t)X % 16 == 0) && (ldx % 4 == 0);
   if (!by_col) {
     q.vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
-    // only short rows (at most 1024 values, 4 float4 per lane): the kernel's
-    // registers are the largest of its bodies', and longer rows would halve
-    // the workgroups a CU holds for every job of the launch
+    // The kernel's registers are the largest of its bodies': rows of up to
+    // 1024 values run the general body (4 float4 per lane), longer ones up to
+    // 3072 values only the aligned-row body (12 float4 per lane, no more
+    // registers than the column bodies); other rows would cut the workgroups
+    // a CU holds for every job of the launch.
     const int vpl = rows_wave_vpl(cols);
-    if (vpl == 0 || vpl > 4) return false;
-    q.kind = QK_ROWS_WAVE; q.param = vpl;
+    if (vpl == 0) return false;
+    if (vpl > 4) {
+      if (vpl > 12 || !q.vec_in || !q.vec_out || (cols & 3) != 0) return false;
+      q.kind = QK_ROWS_VEC;
+    } else {
+      q.kind = QK_ROWS_WAVE;
+    }
+    q.param = vpl;
     q.blocks = (int)((rows + 15) / 16);   // 16 waves per workgroup, a wave per row
     return true;
   }

@@ -33,11 +33,15 @@ def _x(seed, rows, cols):
 
 # (rows, cols, by_col, fmt): rows passes of every length class (wave path,
 # block path, long rows), column passes on the register path and on the tall
-# multi-kernel path, int4 and pow2 formats, empty lines
+# multi-kernel path, int4 and pow2 formats, empty lines.  Aligned rows of
+# 1025-3072 values run inside the batch (8 and 12 float4 per lane); a length
+# that is not a multiple of 4 runs its own kernel.
 JOBS = [(8192, 768, False, 0), (768, 3072, True, 0), (3072, 768, True, 0), (100, 1, False, 0),
         (37, 4000, False, 0), (5, 5000, False, 0), (3, 40000, False, 0), (100, 70, True, 0),
         (9000, 33, True, 0), (64, 300, False, F.POW2), (300, 64, True, F.POW2), (50, 77, False, F.INT4),
-        (77, 50, True, F.INT4), (0, 10, False, 0), (10, 0, False, 0), (0, 10, True, 0), (1, 1, True, 0)]
+        (77, 50, True, F.INT4), (0, 10, False, 0), (10, 0, False, 0), (0, 10, True, 0), (1, 1, True, 0),
+        (8192, 3072, False, 0), (300, 2044, False, 0), (40, 1030, False, 0), (64, 2048, False, F.POW2),
+        (33, 3072, False, F.POW2)]
 
 
 def test_batch_equals_single_calls(g):
@@ -51,7 +55,7 @@ def test_batch_equals_single_calls(g):
         assert torch.equal(Q, Q1), job
         assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), job
     # oracle on a few jobs directly
-    for k in (0, 1, 2, 4, 9):
+    for k in (0, 1, 2, 4, 9, 17, 18, 20):
         X, bc, f = specs[k]
         Q, s = outs[k]
         qo, so = (F.quantize_cols if bc else F.quantize_rows)(X.cpu().numpy(), f)
