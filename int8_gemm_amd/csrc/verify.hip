@@ -307,14 +307,16 @@ inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // ---------------------------------------------------------------------------
 struct QCase { int64_t rows, cols; bool by_col; int fmt; bool batch; };
 struct GCase { int64_t M, N, K; int splits; };
-// the last four int8 cases run as quantize_batch calls (with a second job)
+// the cases marked batch run as quantize_batch calls (with a second job);
+// the aligned rows of 2048 and 3072 values take the batch's long-row body
 const QCase kQCases[] = {{37, 301, false, 0, false},  {5, 4500, false, 0, false},
                          {1, 1, false, 0, false},     {300, 37, true, 0, false},
                          {8200, 33, true, 0, false},  {700, 64, true, 0, false},
                          {37, 301, false, FMT_INT4, false},  {300, 37, true, FMT_INT4 | FMT_POW2, false},
                          {64, 100, false, FMT_POW2, false},  {100, 64, true, FMT_POW2, false},
                          {65, 1000, false, 0, true},  {1000, 65, true, 0, true},
-                         {33, 700, false, FMT_POW2, true}, {700, 33, true, 0, true}};
+                         {33, 700, false, FMT_POW2, true}, {700, 33, true, 0, true},
+                         {24, 2048, false, 0, true}, {9, 3072, false, FMT_POW2, true}};
 const GCase kGCases[] = {{17, 33, 15, 0}, {130, 190, 70, 0}, {300, 520, 192, 0},
                          {256, 200, 768, 0}, {64, 64, 4096, 4}};
 constexpr int kGateCfgs = 8;   // tile configurations of the GEMM planner

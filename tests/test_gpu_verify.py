@@ -26,9 +26,9 @@ def test_gate_passes(g):
     rc, rep = g.gate()
     assert rc == 0, (g.load().i8g_status_string(rc), rep)
     assert rep["check"] == 0
-    # quantize cases (14) + GEMM cases x configurations (5 x 8) + int4 GEMMs x 2 paths (3 x 2)
+    # quantize cases (16) + GEMM cases x configurations (5 x 8) + int4 GEMMs x 2 paths (3 x 2)
     # + requant (1)
-    assert rep["cases"] >= 14 + 5 * 8 + 3 * 2 + 1
+    assert rep["cases"] >= 16 + 5 * 8 + 3 * 2 + 1
 
 
 def _live_gemm(g, M, N, K, relu, seed):
