@@ -96,8 +96,11 @@ def test_quantize_rows_unaligned(g):
     assert_bits(s.cpu().numpy(), so, "scale")
 
 
+# includes the GPT-2 weights' bands (768 rows: 32 columns, 3072 rows: 8) and
+# the same widths with a ragged last band
 QC_SHAPES = [(1, 1), (5, 3), (300, 17), (768, 64), (1000, 100), (130, 257), (3072, 40), (65, 1030),
-             (512, 300), (8192, 70), (8193, 33), (2, 5000)]
+             (512, 300), (8192, 70), (8193, 33), (2, 5000), (768, 3072), (3072, 768), (1000, 2100),
+             (3000, 700)]
 
 
 @pytest.mark.parametrize("rows,cols", QC_SHAPES)
