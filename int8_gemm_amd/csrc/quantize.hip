@@ -961,19 +961,21 @@ qcols_reg_kernel(const float* __restrict__ X, int64_t rows, int64_t cols, int64_
 }
 
 // Band width for the one-kernel path: as wide as the registers allow (BC *
-// rows <= 32768) while leaving at least 64 workgroups; 0 = use the
+// rows <= 32768) while leaving at least min_wgs workgroups; 0 = use the
 // multi-kernel path (more than 8192 rows).  Wider bands read longer pieces
-// of each row (fewer L2 requests per byte); with at least 64 rather than 128
-// workgroups the GPT-2 weights take 32 (768 rows) and 8 (3072 rows) columns
-// per band instead of 16 and 4: MLP step 0.4%, transformer layer 0.9% and LM
-// head 0.6% faster, measured back to back on one box.
-static int qcols_band(int64_t rows, int64_t cols) {
+// of each row (fewer L2 requests per byte) with fewer workgroups.  A launch
+// of its own keeps at least 128 (768x3072: 16 columns per band, 5.0 us
+// against 6.7 with 32); a job of quantize_batch, which shares the launch,
+// at least 64 (the GPT-2 weights take 32 and 8 columns instead of 16 and 4:
+// MLP step 0.4%, transformer layer 0.9%, LM head 0.6% faster, measured back
+// to back on one box).
+static int qcols_band(int64_t rows, int64_t cols, int min_wgs = 128) {
   if (rows > QCR_MAX_ELEMS / 4) return 0;
   int bc = 4;
   for (int c = 64; c >= 4; c >>= 1) {
     if ((int64_t)c * rows > QCR_MAX_ELEMS) continue;
     bc = c;
-    if ((cols + c - 1) / c >= 64) break;
+    if ((cols + c - 1) / c >= min_wgs) break;
   }
   return bc;
 }
@@ -1256,7 +1258,7 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
     return true;
   }
   q.vec_out = ((uintptr_t)Q % 16 == 0) && (ldq % 16 == 0);
-  const int bc = qcols_band(rows, cols);
+  const int bc = qcols_band(rows, cols, 64);
   if (bc == 0 || qcols_path_requested() == 1) return false;   // the multi-kernel path
   // the cooperative path needs a launch of its own; a pass the whole-line
   // kernels would take alone stays a band job here, where it overlaps the
