@@ -35,13 +35,15 @@ def _x(seed, rows, cols):
 # block path, long rows), column passes on the register path and on the tall
 # multi-kernel path, int4 and pow2 formats, empty lines.  Aligned rows of
 # 1025-3072 values run inside the batch (8 and 12 float4 per lane); a length
-# that is not a multiple of 4 runs its own kernel.
+# that is not a multiple of 4 runs its own kernel.  Column jobs of the GPT-2
+# weights' shapes take wider bands in the batch than in a call of their own
+# (32 and 8 columns against 16 and 4), in every format.
 JOBS = [(8192, 768, False, 0), (768, 3072, True, 0), (3072, 768, True, 0), (100, 1, False, 0),
         (37, 4000, False, 0), (5, 5000, False, 0), (3, 40000, False, 0), (100, 70, True, 0),
         (9000, 33, True, 0), (64, 300, False, F.POW2), (300, 64, True, F.POW2), (50, 77, False, F.INT4),
         (77, 50, True, F.INT4), (0, 10, False, 0), (10, 0, False, 0), (0, 10, True, 0), (1, 1, True, 0),
         (8192, 3072, False, 0), (300, 2044, False, 0), (40, 1030, False, 0), (64, 2048, False, F.POW2),
-        (33, 3072, False, F.POW2)]
+        (33, 3072, False, F.POW2), (768, 3072, True, F.INT4), (3072, 768, True, F.POW2)]
 
 
 def test_batch_equals_single_calls(g):
@@ -55,11 +57,14 @@ def test_batch_equals_single_calls(g):
         assert torch.equal(Q, Q1), job
         assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), job
     # oracle on a few jobs directly
-    for k in (0, 1, 2, 4, 9, 17, 18, 20):
+    for k in (0, 1, 2, 4, 9, 17, 18, 20, 22, 23):
         X, bc, f = specs[k]
         Q, s = outs[k]
         qo, so = (F.quantize_cols if bc else F.quantize_rows)(X.cpu().numpy(), f)
-        assert np.array_equal(Q.cpu().numpy(), qo) and np.array_equal(s.cpu().numpy(), so), JOBS[k]
+        Qn = Q.cpu().numpy()
+        if f & F.INT4:                     # packed lines, two codes per byte
+            Qn, qo = Qn.view(np.uint8), F.pack_int4(qo)
+        assert np.array_equal(Qn, qo) and np.array_equal(s.cpu().numpy(), so), JOBS[k]
 
 
 def test_batch_many_jobs_several_launches(g):
