@@ -1242,9 +1242,9 @@ bool plan_qjob(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* 
     q.vec_out = ((uintptr_t)Q % 4 == 0) && (ldq % 4 == 0);
     // The kernel's registers are the largest of its bodies': rows of up to
     // 1024 values run the general body (4 float4 per lane), longer ones up to
-    // 3072 values only the aligned-row body (12 float4 per lane, no more
-    // registers than the column bodies); other rows would cut the workgroups
-    // a CU holds for every job of the launch.
+    // 3072 values only the aligned-row body (12 float4 per lane; the launch
+    // stays within 64 registers, two workgroups per CU); other rows would cut
+    // the workgroups a CU holds for every job of the launch.
     const int vpl = rows_wave_vpl(cols);
     if (vpl == 0) return false;
     if (vpl > 4) {
