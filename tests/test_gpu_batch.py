@@ -70,6 +70,8 @@ def test_batch_equals_single_calls(g):
 def test_batch_many_jobs_several_launches(g):
     """More jobs than one launch holds (24): the batch is split."""
     specs = [(_x(100 + i, 17 + 13 * i, 31 + 7 * i), i % 2 == 1, 0) for i in range(53)]
+    # aligned long rows (the batch's long-row body) in the later launches too
+    specs += [(_x(200 + i, 3 + i, 1024 + 512 * i), False, 0) for i in range(1, 5)]
     say("batch of", len(specs))
     outs = g.quantize_batch(specs)
     torch.cuda.synchronize()
