@@ -154,7 +154,9 @@ int quantize_cols_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx,
  * passes that fit one kernel run in a single launch (24 at most per launch)
  * and share the chip, which matters for the many small passes of a step
  * (weights, skinny activations) whose time is mostly latency; the others
- * (int4 row passes, column passes over more than 8192 rows) are
+ * (int4 row passes, rows of more than 3072 values, rows of more than 1024
+ * values that are not 16-byte aligned with a length that is a multiple of 4,
+ * column passes over more than 8192 rows or of at least 256 MiB) are
  * enqueued one by one on the same stream.  Every output is byte for byte
  * that of the single call.
  *   jobs  host array of n descriptions; by_col = 0 is quantize_rows_fmt,
